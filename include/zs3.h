@@ -1,0 +1,296 @@
+/*
+ * zs3.h -- C ABI of the ZeRO-3 shard-step library (libzs3.so, HIP on gfx950).
+ *
+ * One GPU's share of a ZeRO stage-3 data-parallel training step.  The N
+ * data-parallel ranks are N "virtual ranks": every buffer a real rank would
+ * receive from its peers is an ordinary device buffer here, so the
+ * library's kernels are exactly the local work of a rank around the
+ * collectives.
+ *
+ * Pages cited (titles, then the section of each passage):
+ *   [codex]  "03 · ZeRO-3: parameter sharding and the all-gather schedule"
+ *            (DeepSpeed chapter, ai-reference-codex.pages.dev)
+ *   [csdn]   "DeepSpeed ZeRO Stage 3: parameter partitioning ..." (adg.csdn.net)
+ *   [llmnex] "ZeRO-3 core flow: the setting that also shards the parameters"
+ *            (llmnex.top)
+ *
+ * Conventions shared by every call
+ *   - Element counts and offsets are in elements of the buffer's type.
+ *   - 16-bit buffers (parameters, gradients, shards, chunks) hold fp16 or
+ *     bf16 values, selected by `dtype`; fp32 buffers hold float.
+ *   - Device pointers ("dev") are caller-owned device memory (for example
+ *     torch tensors' data pointers).  They must be 2-byte aligned (16-bit
+ *     data) or 4-byte aligned (fp32); 16-byte alignment enables the
+ *     128-bit fast paths but is not required.
+ *   - Host arrays ("host") are read before the call returns.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call that
+ *     takes a stream only enqueues work on it and returns; none
+ *     synchronises.  Outputs are ready when the stream reaches that point.
+ *   - All arguments are validated before any work is enqueued: on an error
+ *     nothing is enqueued and the return value says why; zs3_last_error()
+ *     gives a message (thread-local).  Nothing throws across the ABI.
+ *   - A layout caches small device tables (segment and work lists, keyed by
+ *     the call's parameters and pointers).  The first call with a new key
+ *     allocates and uploads its table synchronously; later identical calls
+ *     reuse it.  Cached tables are freed only by zs3_layout_destroy, which
+ *     first waits for the device to go idle.
+ *   - Calls on one layout from several host threads must be serialised by
+ *     the caller.  zs3_grad_norm keeps per-layout scratch: two norm calls
+ *     on one layout that overlap on different streams race.
+ */
+#ifndef ZS3_H
+#define ZS3_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZS3_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define ZS3_API __attribute__((visibility("default")))
+#else
+#define ZS3_API
+#endif
+
+typedef int32_t zs3_status;
+
+enum {
+    ZS3_OK = 0,
+    ZS3_EINVAL = -1,     /* null pointer, size, rank or world size out of range, numel < 1 */
+    ZS3_EDTYPE = -2,     /* dtype is neither ZS3_FP16 nor ZS3_BF16 */
+    ZS3_EDUPID = -3,     /* a ds_id appears twice */
+    ZS3_ENOTFOUND = -4,  /* a ds_id is not in the layout */
+    ZS3_EPERSIST = -5,   /* a persistent (never partitioned) parameter in a gather request */
+    ZS3_EALIAS = -6,     /* an output overlaps an input it must not overlap */
+    ZS3_EHIP = -7,       /* a HIP runtime call or kernel launch failed */
+    ZS3_ENOMEM = -8      /* host or device allocation failed */
+};
+
+enum { ZS3_FP16 = 1, ZS3_BF16 = 2 };          /* 16-bit storage types */
+enum { ZS3_PACK = 1, ZS3_UNPACK = 2 };        /* zs3_gather_coalesced modes (bit mask) */
+enum { ZS3_GATHER_BUCKETS = 1, ZS3_REDUCE_BUCKETS = 2 };
+
+typedef struct zs3_layout* zs3_layout_t;
+
+/* Adam hyperparameters.  The fp32 constants of a step (lr, beta1, beta2,
+ * 1-beta1, 1-beta2, 1-beta1^step, 1-beta2^step, eps, lr*weight_decay) are
+ * each computed in double from these and rounded once to float. */
+typedef struct {
+    double lr;
+    double beta1;
+    double beta2;
+    double eps;
+    double weight_decay;   /* decoupled: w -= (lr*wd)*w before the update */
+    int64_t step;          /* t >= 1 */
+} zs3_adam_params;
+
+/* ---------------------------------------------------------------- misc */
+
+ZS3_API int32_t zs3_abi_version(void);
+ZS3_API const char* zs3_status_str(zs3_status s);
+/* Message of the last failed call on this host thread ("" if none). */
+ZS3_API const char* zs3_last_error(void);
+
+/* ------------------------------------------------------------- layout
+ * [codex] 3.1: rank r holds elements [r*partition_size, (r+1)*partition_size)
+ * of every flattened parameter.  [codex] 5.3: parameters with
+ * numel < persistence_threshold are never partitioned: every rank holds
+ * them whole.  [codex] 5.2: the coalesced gather orders parameters by
+ * ds_id, so a rank's flat shard lists parameters in ascending ds_id.
+ *
+ * partition_size = ceil(numel / world_size) for partitioned parameters and
+ * numel for persistent ones; positions >= numel of the padded flat
+ * parameter are zero padding.  A rank's flat shard (and its flat gradient
+ * and fp32 state) has shard_numel = sum of partition sizes elements, each
+ * parameter at shard_offset = prefix sum in ascending ds_id.
+ *
+ * zs3_layout_create: ds_id[i] >= 0 unique, numel[i] >= 1, n_params >= 0,
+ * world_size >= 1, threshold >= 0 (host arrays of n_params).  Host-only:
+ * no device work.  *out receives a handle to release with
+ * zs3_layout_destroy.
+ */
+ZS3_API zs3_status zs3_layout_create(int32_t world_size, int64_t persistence_threshold,
+                             int32_t n_params, const int64_t* ds_id, const int64_t* numel,
+                             zs3_layout_t* out);
+/* Waits for the device to go idle, frees cached device tables and the handle.
+ * NULL is ignored. */
+ZS3_API void zs3_layout_destroy(zs3_layout_t layout);
+
+/* Counts and per-parameter facts; any output pointer may be NULL. */
+ZS3_API zs3_status zs3_layout_info(zs3_layout_t layout, int32_t* world_size, int64_t* persistence_threshold,
+                           int32_t* n_params, int64_t* shard_numel, int64_t* bytes_per_rank);
+/* bytes_per_rank = 16 * shard_numel: 16-bit param + 16-bit grad + fp32
+ * master, momentum, variance per held element ([codex] section 1, 16 Psi/N;
+ * [llmnex] section 1, 2 + 2 + 12 bytes). */
+
+/* The index-th parameter in ascending ds_id order (0 <= index < n_params). */
+ZS3_API zs3_status zs3_layout_param_at(zs3_layout_t layout, int32_t index, int64_t* ds_id, int64_t* numel,
+                               int64_t* partition_size, int32_t* persistent, int64_t* shard_offset);
+/* The same facts by ds_id. */
+ZS3_API zs3_status zs3_layout_param(zs3_layout_t layout, int64_t ds_id, int64_t* numel,
+                            int64_t* partition_size, int32_t* persistent, int64_t* shard_offset);
+/* [lo, hi) of the flattened parameter that `rank` holds real data for
+ * (hi == lo when the rank's range lies wholly in the padding). */
+ZS3_API zs3_status zs3_layout_own_range(zs3_layout_t layout, int64_t ds_id, int32_t rank,
+                                int64_t* lo, int64_t* hi);
+
+/* ------------------------------------------------------- host planning
+ * Bucket plans.  kind = ZS3_GATHER_BUCKETS: non-persistent parameters in
+ * ascending ds_id, filled up to `limit` full elements ([codex] 5.2: a
+ * prefetch fills up to the prefetch bucket size).  kind =
+ * ZS3_REDUCE_BUCKETS: every parameter in descending ds_id (backward
+ * arrival order), filled up to `limit` full elements ([codex] 6.2: grads
+ * collect in a bucket that is reduced when full).  Greedy: a bucket closes
+ * before a parameter that would take it past `limit`, unless it is empty.
+ * Outputs: *n_buckets; bucket b is ds_ids_out[starts[b] .. starts[b+1]).
+ * starts (host) needs n_buckets+1 entries and ds_ids_out (host) n_params;
+ * if cap (the capacity of starts) is too small, ZS3_EINVAL is returned with
+ * *n_buckets set to the number needed.
+ */
+ZS3_API zs3_status zs3_plan_buckets(zs3_layout_t layout, int32_t kind, int64_t limit, int32_t cap,
+                            int32_t* n_buckets, int32_t* starts, int64_t* ds_ids_out);
+
+/* Sub-groups ([codex] 6.1: the optimizer splits the parameters into
+ * sub-groups of at most sub_group_size elements, its unit of stepping):
+ * contiguous [begin, end) ranges of the rank's flat shard, greedy in
+ * ascending ds_id, counted in shard elements, never splitting a parameter.
+ * begin_end (host) receives 2*n_groups values; cap is its capacity in
+ * groups (see zs3_plan_buckets for the too-small case). */
+ZS3_API zs3_status zs3_sub_groups(zs3_layout_t layout, int64_t sub_group_size, int32_t cap,
+                          int32_t* n_groups, int64_t* begin_end);
+
+/* Sizes of a gather bucket: chunk_numel = sum of partition sizes (one
+ * rank's chunk), full_numel = sum of numels (the gathered flat buffer). */
+ZS3_API zs3_status zs3_bucket_sizes(zs3_layout_t layout, int32_t n, const int64_t* ds_ids,
+                            int64_t* chunk_numel, int64_t* full_numel);
+
+/* ---------------------------------------------------- (1) partition
+ * [codex] 3.1: right after construction each parameter's own element range
+ * is copied into the rank's shard; [codex] 5.3: persistent parameters are
+ * copied whole.
+ *
+ * For each of the n requested parameters (ds_ids, host, any order, no
+ * duplicates), copies the rank's own range of full_params[i] (dev, numel
+ * 16-bit elements, the flattened parameter) to shard_flat[shard_offset ..]
+ * (dev, shard_numel elements) and writes 0 to the padding positions of its
+ * partition.  Other positions of shard_flat are not touched.
+ */
+ZS3_API zs3_status zs3_partition(zs3_layout_t layout, int32_t rank, int32_t dtype, int32_t n,
+                         const int64_t* ds_ids, const void* const* full_params,
+                         void* shard_flat, void* stream);
+
+/* ------------------------------------------ (2) all_gather_coalesced
+ * [codex] 5.2: the shards of the requested group are ordered by ds_id and
+ * joined into one flat buffer, one collective gathers the whole group, and
+ * each parameter's data becomes a view of the gathered flat buffer.
+ * [codex] section 7: a wrong order silently yields wrong parameters, so the
+ * order is fixed by ds_id whatever the request order.
+ *
+ * The bucket is the n parameters ds_ids (host, any order, no duplicates,
+ * none persistent).  Let j run over them in ascending ds_id, c_j = prefix
+ * sum of partition sizes, f_j = prefix sum of numels.
+ *   mode & ZS3_PACK:   own_chunk[c_j + k] = shard_flat[shard_offset_j + k],
+ *                      k < partition_size_j (padding included).
+ *                      shard_flat: dev, the rank's flat shard.
+ *                      own_chunk: dev, chunk_numel elements.
+ *   mode & ZS3_UNPACK: full_flat[f_j + v*ps_j + k] = rank_chunks[v][c_j + k]
+ *                      for every rank v and every k with v*ps_j + k < numel_j
+ *                      (padding is dropped).  rank_chunks: host array of N
+ *                      dev pointers, each chunk_numel elements (the
+ *                      all-gather's rank-major output, one pointer per
+ *                      rank).  full_flat: dev, full_numel elements.
+ *                      full_offsets (host, n entries, may be NULL) receives
+ *                      f_j for the i-th requested ds_id: parameter i is the
+ *                      view full_flat + full_offsets[i] of numel_i elements.
+ * With both bits the pack runs first; rank_chunks[rank] may then be
+ * own_chunk.  Unused pointers may be NULL.
+ */
+ZS3_API zs3_status zs3_gather_coalesced(zs3_layout_t layout, int32_t rank, int32_t dtype, int32_t mode,
+                                int32_t n, const int64_t* ds_ids, const void* shard_flat,
+                                void* own_chunk, const void* const* rank_chunks, void* full_flat,
+                                int64_t* full_offsets, void* stream);
+
+/* ------------------------------------------ (3) local reduce-scatter
+ * [codex] 6.2: the contiguous-gradient path all-reduces the bucket and each
+ * rank keeps only its own interval, written into the one contiguous flat
+ * gradient buffer; no full gradient is ever kept.  [csdn] core algorithm
+ * step 3: the reduction sums and averages, each GPU keeps its part.
+ *
+ * For the n parameters ds_ids (host, any order, no duplicates; persistent
+ * ones allowed: their "own slice" is the whole gradient), with
+ * [lo_i, hi_i) the rank's own range of parameter i:
+ *   grad_flat[shard_offset_i + k] =
+ *       round16( (((0 + g_0[k]) + g_1[k]) + ... + g_{N-1}[k]) / N )
+ * for k < hi_i - lo_i, with g_v = src[i*N + v] and every + and / one fp32
+ * operation, round16 = round to nearest even into dtype; the remaining
+ * positions k < partition_size_i (padding) are written as 0.
+ * src: host array of n*N dev pointers; src[i*N + v] points at element lo_i
+ * of virtual rank v's gradient of parameter i (it may be NULL when
+ * hi_i == lo_i).  This serves whole per-rank gradient buckets as well as
+ * slice-only storage.  grad_flat: dev, shard_numel elements.  The sources
+ * must not overlap the written range of grad_flat.
+ */
+ZS3_API zs3_status zs3_reduce_scatter_local(zs3_layout_t layout, int32_t rank, int32_t dtype, int32_t n,
+                                    const int64_t* ds_ids, const void* const* src, void* grad_flat,
+                                    void* stream);
+
+/* ------------------------------------------------ (4) global grad norm
+ * [codex] 6.3: every sub-group is unscaled and clipped with the one global
+ * norm.  [llmnex] pitfall 1: each card sees only its own part of the norm;
+ * the partial sums must be combined so that every partition uses the same
+ * coefficient.
+ *
+ * Partial step (always): sumsq[rank] = sum over the rank's real partitioned
+ * gradient elements of x*x, sumsq[N] = the same over the persistent
+ * gradients (identical on every rank, counted once); x is the element
+ * widened exactly to double and the sums are in double.  grad_flat: dev,
+ * shard_numel 16-bit elements.  sumsq: dev, N+1 doubles.
+ * Finalize step (finalize != 0): total = sumsq[0] + ... + sumsq[N-1] (in
+ * rank order) + sumsq[N]; *norm_out = sqrt(total); *nonfinite = total is
+ * inf or NaN; coef = min(1, max_norm / (norm + 1e-6));
+ * *scale_out = (float)(coef / loss_scale).  The caller supplies the other
+ * ranks' sumsq entries (in a multi-GPU run they arrive by an all-reduce of
+ * N+1 doubles).  norm_out (double), scale_out (float), nonfinite (int32)
+ * are dev pointers; they may be NULL when finalize == 0.
+ * Requires max_norm > 0 and loss_scale > 0.
+ */
+ZS3_API zs3_status zs3_grad_norm(zs3_layout_t layout, int32_t rank, int32_t dtype, const void* grad_flat,
+                         double* sumsq, int32_t finalize, double max_norm, double loss_scale,
+                         double* norm_out, float* scale_out, int32_t* nonfinite, void* stream);
+
+/* ----------------------------------------- (5) fused Adam + 16-bit cast
+ * [codex] 6.3: per sub-group, the rank's fp32 partition is stepped by the
+ * real optimizer (it sees only this rank's shard) and the result is written
+ * back into the 16-bit shard.  [llmnex] section 1: the optimizer state is an
+ * fp32 master weight, momentum and variance per element.
+ *
+ * For every real (non-padding) position e of the rank's flat shard in
+ * [begin, end), one IEEE fp32 operation per step, no contraction:
+ *   g = float(grad_flat[e]) * (*scale)
+ *   if wd != 0: w = w - (lr*wd) * w
+ *   m = b1*m + (1-b1)*g ;  v = b2*v + (1-b2)*(g*g)
+ *   den = sqrt(v / (1-b2^t)) + eps
+ *   w = w - lr * ((m / (1-b1^t)) / den)
+ *   shard_flat[e] = round16(w)
+ * with w = master[e], m = exp_avg[e], v = exp_avg_sq[e] (Kingma & Ba's Adam
+ * with bias correction; the pages name the state but print no formula).
+ * Padding positions are not touched.  If nonfinite is not NULL and
+ * *nonfinite != 0 the kernel writes nothing.
+ * master, exp_avg, exp_avg_sq: dev fp32, grad_flat and shard_flat: dev
+ * 16-bit, all the rank's whole flat arrays (shard_numel elements, indexed
+ * from 0).  scale: dev float (from zs3_grad_norm).  hp: host.
+ * 0 <= begin <= end <= shard_numel.  The five arrays must not overlap.
+ */
+ZS3_API zs3_status zs3_adam_step(zs3_layout_t layout, int32_t rank, int32_t dtype, int64_t begin, int64_t end,
+                         float* master, float* exp_avg, float* exp_avg_sq, const void* grad_flat,
+                         void* shard_flat, const float* scale, const int32_t* nonfinite,
+                         const zs3_adam_params* hp, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZS3_H */

@@ -1,0 +1,279 @@
+"""Python binding of libzs3, the ZeRO-3 shard-step library for MI355X.
+
+Argument marshalling only: every function below has the name of a C entry
+point in ``include/zs3.h`` and forwards to it through ctypes.  Device
+buffers may be given as torch tensors (their data pointers are passed) or as
+raw integer device addresses; ``stream`` may be a ``torch.cuda.Stream``, a
+raw ``hipStream_t`` integer, or ``None`` for torch's current stream.  A
+non-zero status raises ``Zs3Error``.  If the shared library has not been
+built, the first call raises ``RuntimeError`` -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzs3.so")
+
+ZS3_OK = 0
+ZS3_EINVAL = -1
+ZS3_EDTYPE = -2
+ZS3_EDUPID = -3
+ZS3_ENOTFOUND = -4
+ZS3_EPERSIST = -5
+ZS3_EALIAS = -6
+ZS3_EHIP = -7
+ZS3_ENOMEM = -8
+
+ZS3_FP16 = 1
+ZS3_BF16 = 2
+ZS3_PACK = 1
+ZS3_UNPACK = 2
+ZS3_GATHER_BUCKETS = 1
+ZS3_REDUCE_BUCKETS = 2
+
+DTYPES = {"fp16": ZS3_FP16, "bf16": ZS3_BF16}
+
+# Every exported symbol of include/zs3.h.
+EXPORTS = (
+    "zs3_abi_version", "zs3_status_str", "zs3_last_error",
+    "zs3_layout_create", "zs3_layout_destroy", "zs3_layout_info", "zs3_layout_param_at",
+    "zs3_layout_param", "zs3_layout_own_range", "zs3_plan_buckets", "zs3_sub_groups",
+    "zs3_bucket_sizes", "zs3_partition", "zs3_gather_coalesced", "zs3_reduce_scatter_local",
+    "zs3_grad_norm", "zs3_adam_step",
+)
+
+
+class Zs3Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"zs3 status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+class zs3_adam_params(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_double),
+        ("beta1", ctypes.c_double),
+        ("beta2", ctypes.c_double),
+        ("eps", ctypes.c_double),
+        ("weight_decay", ctypes.c_double),
+        ("step", ctypes.c_int64),
+    ]
+
+
+_c_i32 = ctypes.c_int32
+_c_i64 = ctypes.c_int64
+_c_p = ctypes.c_void_p
+_p_i64 = ctypes.POINTER(ctypes.c_int64)
+_p_i32 = ctypes.POINTER(ctypes.c_int32)
+
+_SIGNATURES = {
+    "zs3_abi_version": (_c_i32, []),
+    "zs3_status_str": (ctypes.c_char_p, [_c_i32]),
+    "zs3_last_error": (ctypes.c_char_p, []),
+    "zs3_layout_create": (_c_i32, [_c_i32, _c_i64, _c_i32, _p_i64, _p_i64, ctypes.POINTER(_c_p)]),
+    "zs3_layout_destroy": (None, [_c_p]),
+    "zs3_layout_info": (_c_i32, [_c_p, _p_i32, _p_i64, _p_i32, _p_i64, _p_i64]),
+    "zs3_layout_param_at": (_c_i32, [_c_p, _c_i32, _p_i64, _p_i64, _p_i64, _p_i32, _p_i64]),
+    "zs3_layout_param": (_c_i32, [_c_p, _c_i64, _p_i64, _p_i64, _p_i32, _p_i64]),
+    "zs3_layout_own_range": (_c_i32, [_c_p, _c_i64, _c_i32, _p_i64, _p_i64]),
+    "zs3_plan_buckets": (_c_i32, [_c_p, _c_i32, _c_i64, _c_i32, _p_i32, _p_i32, _p_i64]),
+    "zs3_sub_groups": (_c_i32, [_c_p, _c_i64, _c_i32, _p_i32, _p_i64]),
+    "zs3_bucket_sizes": (_c_i32, [_c_p, _c_i32, _p_i64, _p_i64, _p_i64]),
+    "zs3_partition": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _p_i64, ctypes.POINTER(_c_p), _c_p, _c_p]),
+    "zs3_gather_coalesced": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _p_i64, _c_p, _c_p,
+                                      ctypes.POINTER(_c_p), _c_p, _p_i64, _c_p]),
+    "zs3_reduce_scatter_local": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _p_i64, ctypes.POINTER(_c_p),
+                                          _c_p, _c_p]),
+    "zs3_grad_norm": (_c_i32, [_c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, ctypes.c_double,
+                               ctypes.c_double, _c_p, _c_p, _c_p, _c_p]),
+    "zs3_adam_step": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
+                               _c_p, _c_p, ctypes.POINTER(zs3_adam_params), _c_p]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libzs3.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m zero_sharded_state_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+# ------------------------------------------------------------- marshalling
+
+def _check(status: int) -> None:
+    if status != ZS3_OK:
+        raise Zs3Error(status, lib().zs3_last_error().decode(errors="replace"))
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(s, int):
+        return s
+    return int(s.cuda_stream)
+
+
+def _i64s(vals: Sequence[int]):
+    arr = (ctypes.c_int64 * max(1, len(vals)))(*[int(v) for v in vals])
+    return arr
+
+
+def _ptrs(vals: Sequence) -> ctypes.Array:
+    return (ctypes.c_void_p * max(1, len(vals)))(*[_ptr(v) for v in vals])
+
+
+def _dtype(d) -> int:
+    return DTYPES[d] if isinstance(d, str) else int(d)
+
+
+def _hp(hp) -> zs3_adam_params:
+    if isinstance(hp, zs3_adam_params):
+        return hp
+    if isinstance(hp, dict):
+        return zs3_adam_params(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp.get("weight_decay", 0.0),
+                               int(hp["step"]))
+    return zs3_adam_params(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, int(hp.step))
+
+
+# ------------------------------------------------------------------- calls
+
+def zs3_abi_version() -> int:
+    return lib().zs3_abi_version()
+
+
+def zs3_status_str(status: int) -> str:
+    return lib().zs3_status_str(status).decode()
+
+
+def zs3_last_error() -> str:
+    return lib().zs3_last_error().decode(errors="replace")
+
+
+def zs3_layout_create(world_size: int, persistence_threshold: int, ds_ids: Sequence[int],
+                      numels: Sequence[int]) -> int:
+    h = ctypes.c_void_p()
+    _check(lib().zs3_layout_create(world_size, int(persistence_threshold), len(ds_ids), _i64s(ds_ids),
+                                   _i64s(numels), ctypes.byref(h)))
+    return h.value
+
+
+def zs3_layout_destroy(layout: int) -> None:
+    lib().zs3_layout_destroy(layout)
+
+
+def zs3_layout_info(layout: int) -> dict:
+    w, np_ = ctypes.c_int32(), ctypes.c_int32()
+    t, s, b = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().zs3_layout_info(layout, ctypes.byref(w), ctypes.byref(t), ctypes.byref(np_),
+                                 ctypes.byref(s), ctypes.byref(b)))
+    return {"world_size": w.value, "persistence_threshold": t.value, "n_params": np_.value,
+            "shard_numel": s.value, "bytes_per_rank": b.value}
+
+
+def zs3_layout_param_at(layout: int, index: int) -> dict:
+    d, n, ps, off = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    pers = ctypes.c_int32()
+    _check(lib().zs3_layout_param_at(layout, index, ctypes.byref(d), ctypes.byref(n), ctypes.byref(ps),
+                                     ctypes.byref(pers), ctypes.byref(off)))
+    return {"ds_id": d.value, "numel": n.value, "partition_size": ps.value, "persistent": bool(pers.value),
+            "shard_offset": off.value}
+
+
+def zs3_layout_param(layout: int, ds_id: int) -> dict:
+    n, ps, off = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    pers = ctypes.c_int32()
+    _check(lib().zs3_layout_param(layout, ds_id, ctypes.byref(n), ctypes.byref(ps), ctypes.byref(pers),
+                                  ctypes.byref(off)))
+    return {"ds_id": ds_id, "numel": n.value, "partition_size": ps.value, "persistent": bool(pers.value),
+            "shard_offset": off.value}
+
+
+def zs3_layout_own_range(layout: int, ds_id: int, rank: int) -> Tuple[int, int]:
+    lo, hi = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().zs3_layout_own_range(layout, ds_id, rank, ctypes.byref(lo), ctypes.byref(hi)))
+    return lo.value, hi.value
+
+
+def zs3_plan_buckets(layout: int, kind: int, limit: int) -> List[List[int]]:
+    n_params = zs3_layout_info(layout)["n_params"]
+    cap = n_params + 1
+    nb = ctypes.c_int32()
+    starts = (ctypes.c_int32 * cap)()
+    ids = (ctypes.c_int64 * max(1, n_params))()
+    _check(lib().zs3_plan_buckets(layout, kind, int(limit), cap, ctypes.byref(nb), starts, ids))
+    return [list(ids[starts[b]:starts[b + 1]]) for b in range(nb.value)]
+
+
+def zs3_sub_groups(layout: int, sub_group_size: int) -> List[Tuple[int, int]]:
+    cap = max(1, zs3_layout_info(layout)["n_params"])
+    ng = ctypes.c_int32()
+    be = (ctypes.c_int64 * (2 * cap))()
+    _check(lib().zs3_sub_groups(layout, int(sub_group_size), cap, ctypes.byref(ng), be))
+    return [(be[2 * g], be[2 * g + 1]) for g in range(ng.value)]
+
+
+def zs3_bucket_sizes(layout: int, ds_ids: Sequence[int]) -> Tuple[int, int]:
+    c, f = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().zs3_bucket_sizes(layout, len(ds_ids), _i64s(ds_ids), ctypes.byref(c), ctypes.byref(f)))
+    return c.value, f.value
+
+
+def zs3_partition(layout: int, rank: int, dtype, ds_ids: Sequence[int], full_params: Sequence,
+                  shard_flat, stream=None) -> None:
+    _check(lib().zs3_partition(layout, rank, _dtype(dtype), len(ds_ids), _i64s(ds_ids), _ptrs(full_params),
+                               _ptr(shard_flat), _stream(stream)))
+
+
+def zs3_gather_coalesced(layout: int, rank: int, dtype, mode: int, ds_ids: Sequence[int], shard_flat=None,
+                         own_chunk=None, rank_chunks: Optional[Sequence] = None, full_flat=None,
+                         stream=None) -> List[int]:
+    n = len(ds_ids)
+    offs = (ctypes.c_int64 * max(1, n))()
+    chunks = _ptrs(rank_chunks) if rank_chunks is not None else None
+    _check(lib().zs3_gather_coalesced(layout, rank, _dtype(dtype), mode, n, _i64s(ds_ids), _ptr(shard_flat),
+                                      _ptr(own_chunk), chunks, _ptr(full_flat), offs, _stream(stream)))
+    return list(offs[:n])
+
+
+def zs3_reduce_scatter_local(layout: int, rank: int, dtype, ds_ids: Sequence[int], src: Sequence,
+                             grad_flat, stream=None) -> None:
+    _check(lib().zs3_reduce_scatter_local(layout, rank, _dtype(dtype), len(ds_ids), _i64s(ds_ids), _ptrs(src),
+                                          _ptr(grad_flat), _stream(stream)))
+
+
+def zs3_grad_norm(layout: int, rank: int, dtype, grad_flat, sumsq, finalize: bool, max_norm: float = 1.0,
+                  loss_scale: float = 1.0, norm_out=None, scale_out=None, nonfinite=None, stream=None) -> None:
+    _check(lib().zs3_grad_norm(layout, rank, _dtype(dtype), _ptr(grad_flat), _ptr(sumsq), int(bool(finalize)),
+                               float(max_norm), float(loss_scale), _ptr(norm_out), _ptr(scale_out),
+                               _ptr(nonfinite), _stream(stream)))
+
+
+def zs3_adam_step(layout: int, rank: int, dtype, begin: int, end: int, master, exp_avg, exp_avg_sq, grad_flat,
+                  shard_flat, scale, nonfinite, hp, stream=None) -> None:
+    p = _hp(hp)
+    _check(lib().zs3_adam_step(layout, rank, _dtype(dtype), int(begin), int(end), _ptr(master), _ptr(exp_avg),
+                               _ptr(exp_avg_sq), _ptr(grad_flat), _ptr(shard_flat), _ptr(scale), _ptr(nonfinite),
+                               ctypes.byref(p), _stream(stream)))

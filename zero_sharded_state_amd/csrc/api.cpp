@@ -1,0 +1,820 @@
+// C ABI of libzs3: argument validation, the host-side layout planner, the
+// per-layout cache of device work lists, and the kernel launches.
+//
+// Pages cited: [codex] "03 · ZeRO-3: parameter sharding and the all-gather
+// schedule" (ai-reference-codex), [csdn] "DeepSpeed ZeRO Stage 3: parameter
+// partitioning ..." (adg.csdn.net), [llmnex] "ZeRO-3 core flow" (llmnex.top).
+
+#include "zs3.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <memory>
+#include <new>
+#include <string>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "zs3_internal.hpp"
+
+using namespace zs3;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+zs3_status fail(zs3_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+zs3_status ok() {
+    g_last_error.clear();
+    return ZS3_OK;
+}
+
+// ------------------------------------------------------------- layout
+
+struct Slot {
+    int64_t ds_id;
+    int64_t numel;
+    int64_t ps;          // partition size
+    int64_t offset;      // shard offset
+    bool persistent;
+
+    // [lo, hi) of the flattened parameter that `rank` holds real data for
+    // ([codex] 3.1 element range; [codex] 5.3 persistent = whole).
+    void own_range(int32_t rank, int64_t* lo, int64_t* hi) const {
+        if (persistent) {
+            *lo = 0;
+            *hi = numel;
+            return;
+        }
+        const int64_t a = static_cast<int64_t>(rank) * ps;
+        const int64_t b = std::min(a + ps, numel);
+        *lo = a;
+        *hi = std::max(a, b);
+    }
+    int64_t real(int32_t rank) const {
+        int64_t lo, hi;
+        own_range(rank, &lo, &hi);
+        return hi - lo;
+    }
+};
+
+struct Key {
+    std::vector<int64_t> w;
+    bool operator==(const Key& o) const { return w == o.w; }
+};
+
+struct KeyHash {
+    size_t operator()(const Key& k) const {
+        uint64_t h = 1469598103934665603ull;
+        for (int64_t x : k.w) {
+            uint64_t v = static_cast<uint64_t>(x);
+            for (int i = 0; i < 8; ++i) {
+                h ^= (v >> (8 * i)) & 0xff;
+                h *= 1099511628211ull;
+            }
+        }
+        return static_cast<size_t>(h);
+    }
+};
+
+// A device work list: one allocation holding the tables of one call shape.
+struct Plan {
+    void* dev = nullptr;
+    size_t bytes = 0;
+    int64_t n_pieces = 0;
+    int64_t n_part = 0;           // norm: spans [0, n_part) are partitioned
+    bool co_aligned = true;       // reduce-scatter: every source co-aligned with its dst
+    size_t off_segs = 0, off_pieces = 0, off_srcs = 0, off_scratch = 0;
+
+    template <typename T>
+    T* at(size_t off) const { return reinterpret_cast<T*>(static_cast<char*>(dev) + off); }
+};
+
+enum Op : int64_t { kOpPartition = 1, kOpPack, kOpUnpack, kOpReduce, kOpNorm, kOpAdam };
+
+constexpr size_t kMaxPlans = 1 << 14;
+
+}  // namespace
+
+struct zs3_layout {
+    int32_t world = 1;
+    int64_t threshold = 0;
+    std::vector<Slot> params;                       // ascending ds_id
+    std::unordered_map<int64_t, int32_t> index;     // ds_id -> position
+    int64_t shard_numel = 0;
+    std::unordered_map<Key, Plan, KeyHash> plans;
+
+    ~zs3_layout() { release_plans(); }
+
+    void release_plans() {
+        if (plans.empty()) return;
+        (void)hipDeviceSynchronize();     // no cached table may be freed while a kernel reads it
+        for (auto& kv : plans) {
+            if (kv.second.dev != nullptr) (void)hipFree(kv.second.dev);
+        }
+        plans.clear();
+    }
+};
+
+namespace {
+
+int device_id() {
+    int d = 0;
+    if (hipGetDevice(&d) != hipSuccess) d = -1;
+    return d;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    if (abytes <= 0 || bbytes <= 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + static_cast<uintptr_t>(bbytes) && y < x + static_cast<uintptr_t>(abytes);
+}
+
+zs3_status check_dtype(int32_t dtype) {
+    if (dtype != ZS3_FP16 && dtype != ZS3_BF16) return fail(ZS3_EDTYPE, "dtype %d is not ZS3_FP16 or ZS3_BF16", dtype);
+    return ZS3_OK;
+}
+
+zs3_status check_layout_rank(const zs3_layout* L, int32_t rank) {
+    if (L == nullptr) return fail(ZS3_EINVAL, "layout is NULL");
+    if (rank < 0 || rank >= L->world) return fail(ZS3_EINVAL, "rank %d outside [0, %d)", rank, L->world);
+    return ZS3_OK;
+}
+
+zs3_status check_ptr16(const void* p, const char* what) {
+    if (p == nullptr) return fail(ZS3_EINVAL, "%s is NULL", what);
+    if (!aligned(p, 2)) return fail(ZS3_EINVAL, "%s is not 2-byte aligned", what);
+    return ZS3_OK;
+}
+
+// Resolve a request's ds_ids to layout positions.  order[k] = position in
+// the request of the k-th parameter in ascending ds_id.
+zs3_status resolve(const zs3_layout* L, int32_t n, const int64_t* ds_ids, bool allow_persistent,
+                   std::vector<int32_t>* pos, std::vector<int32_t>* order) {
+    if (n < 0) return fail(ZS3_EINVAL, "n = %d < 0", n);
+    if (n > 0 && ds_ids == nullptr) return fail(ZS3_EINVAL, "ds_ids is NULL");
+    pos->resize(n);
+    std::unordered_set<int64_t> seen;
+    seen.reserve(static_cast<size_t>(n) * 2);
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = L->index.find(ds_ids[i]);
+        if (it == L->index.end()) return fail(ZS3_ENOTFOUND, "ds_id %lld is not in the layout", (long long)ds_ids[i]);
+        if (!seen.insert(ds_ids[i]).second) return fail(ZS3_EDUPID, "ds_id %lld requested twice", (long long)ds_ids[i]);
+        if (!allow_persistent && L->params[it->second].persistent)
+            return fail(ZS3_EPERSIST, "ds_id %lld is persistent (never partitioned, never gathered)",
+                        (long long)ds_ids[i]);
+        (*pos)[i] = it->second;
+    }
+    order->resize(n);
+    for (int32_t i = 0; i < n; ++i) (*order)[i] = i;
+    std::sort(order->begin(), order->end(), [&](int32_t a, int32_t b) { return (*pos)[a] < (*pos)[b]; });
+    return ZS3_OK;
+}
+
+// Split a contiguous segment into workgroup pieces whose starts (after the
+// first) are 16-byte aligned in the destination.
+void add_pieces(std::vector<Piece>* out, int32_t seg, uintptr_t dst_addr, int64_t count, int64_t P) {
+    if (count <= 0) return;
+    const int64_t head = static_cast<int64_t>(((16u - (dst_addr & 15u)) & 15u) >> 1);
+    const int64_t first = std::min(count, head + P);
+    out->push_back(Piece{0, seg, static_cast<int32_t>(first)});
+    for (int64_t b = first; b < count; b += P) out->push_back(Piece{b, seg, static_cast<int32_t>(std::min(P, count - b))});
+}
+
+// Split [begin, begin+count) of a flat array into spans that, after the
+// first, start at multiples of 8 elements when the array base is 16-byte
+// aligned (`head` = elements until the first aligned position).
+void add_spans(std::vector<Span>* out, int64_t begin, int64_t count, int64_t head, int64_t P) {
+    if (count <= 0) return;
+    const int64_t first = std::min(count, head + P);
+    out->push_back(Span{begin, static_cast<int32_t>(first), 0});
+    for (int64_t b = first; b < count; b += P)
+        out->push_back(Span{begin + b, static_cast<int32_t>(std::min(P, count - b)), 0});
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Upload the host tables of a new plan in one allocation.
+zs3_status upload(Plan* plan, const std::vector<std::pair<const void*, size_t>>& parts, size_t scratch_bytes,
+                  std::vector<size_t>* offs) {
+    size_t total = 0;
+    offs->clear();
+    for (const auto& p : parts) {
+        offs->push_back(total);
+        total = align_up(total + p.second, 256);
+    }
+    plan->off_scratch = total;
+    total += scratch_bytes;
+    if (total == 0) total = 256;
+    void* dev = nullptr;
+    if (hipMalloc(&dev, total) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ZS3_ENOMEM, "hipMalloc of a %zu-byte work list failed", total);
+    }
+    std::vector<char> host(total - scratch_bytes, 0);
+    for (size_t i = 0; i < parts.size(); ++i)
+        if (parts[i].second) std::memcpy(host.data() + (*offs)[i], parts[i].first, parts[i].second);
+    if (!host.empty() && hipMemcpy(dev, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipFree(dev);
+        return fail(ZS3_EHIP, "upload of a work list failed");
+    }
+    plan->dev = dev;
+    plan->bytes = total;
+    return ZS3_OK;
+}
+
+zs3_status store_plan(zs3_layout* L, Key&& key, Plan&& plan, Plan** out) {
+    if (L->plans.size() >= kMaxPlans) L->release_plans();
+    auto it = L->plans.emplace(std::move(key), std::move(plan)).first;
+    *out = &it->second;
+    return ZS3_OK;
+}
+
+zs3_status check_grid(int64_t n_pieces) {
+    if (n_pieces * kBlock >= (int64_t(1) << 32)) return fail(ZS3_EINVAL, "request too large for one launch");
+    return ZS3_OK;
+}
+
+zs3_status hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(ZS3_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// ---- copy plans (partition, pack, unpack) --------------------------------
+
+zs3_status build_copy_plan(zs3_layout* L, Key&& key, const std::vector<CopySeg>& segs_in, Plan** out) {
+    // merge segments that continue each other in both source and destination
+    std::vector<CopySeg> segs;
+    for (const CopySeg& s : segs_in) {
+        if (s.count <= 0) continue;
+        if (!segs.empty()) {
+            CopySeg& b = segs.back();
+            const bool dst_next = b.dst + b.count == s.dst;
+            const bool src_next = (b.src == nullptr && s.src == nullptr) ||
+                                  (b.src != nullptr && s.src != nullptr && b.src + b.count == s.src);
+            if (dst_next && src_next) {
+                b.count += s.count;
+                continue;
+            }
+        }
+        segs.push_back(s);
+    }
+    std::vector<Piece> pieces;
+    for (size_t i = 0; i < segs.size(); ++i)
+        add_pieces(&pieces, static_cast<int32_t>(i), reinterpret_cast<uintptr_t>(segs[i].dst), segs[i].count, kCopyPiece);
+    zs3_status s = check_grid(static_cast<int64_t>(pieces.size()));
+    if (s != ZS3_OK) return s;
+    Plan plan;
+    plan.n_pieces = static_cast<int64_t>(pieces.size());
+    std::vector<size_t> offs;
+    s = upload(&plan, {{segs.data(), segs.size() * sizeof(CopySeg)}, {pieces.data(), pieces.size() * sizeof(Piece)}},
+               0, &offs);
+    if (s != ZS3_OK) return s;
+    plan.off_segs = offs[0];
+    plan.off_pieces = offs[1];
+    return store_plan(L, std::move(key), std::move(plan), out);
+}
+
+zs3_status run_copy(const Plan* p, void* stream) {
+    return hip_status(launch_copy(p->at<CopySeg>(p->off_segs), p->at<Piece>(p->off_pieces), p->n_pieces,
+                                  static_cast<hipStream_t>(stream)),
+                      "copy kernel launch");
+}
+
+Plan* find_plan(zs3_layout* L, const Key& k) {
+    auto it = L->plans.find(k);
+    return it == L->plans.end() ? nullptr : &it->second;
+}
+
+}  // namespace
+
+// ======================================================================
+// C ABI
+// ======================================================================
+
+extern "C" {
+
+int32_t zs3_abi_version(void) { return ZS3_ABI_VERSION; }
+
+const char* zs3_status_str(zs3_status s) {
+    switch (s) {
+        case ZS3_OK: return "ok";
+        case ZS3_EINVAL: return "invalid argument";
+        case ZS3_EDTYPE: return "unsupported dtype";
+        case ZS3_EDUPID: return "duplicate ds_id";
+        case ZS3_ENOTFOUND: return "ds_id not in layout";
+        case ZS3_EPERSIST: return "persistent parameter in a gather request";
+        case ZS3_EALIAS: return "overlapping input and output";
+        case ZS3_EHIP: return "HIP error";
+        case ZS3_ENOMEM: return "out of memory";
+        default: return "unknown status";
+    }
+}
+
+const char* zs3_last_error(void) { return g_last_error.c_str(); }
+
+zs3_status zs3_layout_create(int32_t world_size, int64_t persistence_threshold, int32_t n_params,
+                             const int64_t* ds_id, const int64_t* numel, zs3_layout_t* out) {
+    if (out == nullptr) return fail(ZS3_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (world_size < 1) return fail(ZS3_EINVAL, "world_size %d < 1", world_size);
+    if (persistence_threshold < 0) return fail(ZS3_EINVAL, "persistence_threshold < 0");
+    if (n_params < 0) return fail(ZS3_EINVAL, "n_params < 0");
+    if (n_params > 0 && (ds_id == nullptr || numel == nullptr)) return fail(ZS3_EINVAL, "ds_id or numel is NULL");
+    std::unique_ptr<zs3_layout> L(new (std::nothrow) zs3_layout());
+    if (!L) return fail(ZS3_ENOMEM, "layout allocation failed");
+    L->world = world_size;
+    L->threshold = persistence_threshold;
+    std::vector<int32_t> order(n_params);
+    for (int32_t i = 0; i < n_params; ++i) {
+        if (ds_id[i] < 0) return fail(ZS3_EINVAL, "ds_id[%d] = %lld < 0", i, (long long)ds_id[i]);
+        if (numel[i] < 1) return fail(ZS3_EINVAL, "numel[%d] = %lld < 1", i, (long long)numel[i]);
+        order[i] = i;
+    }
+    std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return ds_id[a] < ds_id[b]; });
+    int64_t offset = 0;
+    L->params.reserve(n_params);
+    for (int32_t k = 0; k < n_params; ++k) {
+        const int32_t i = order[k];
+        if (k > 0 && ds_id[order[k - 1]] == ds_id[i]) return fail(ZS3_EDUPID, "duplicate ds_id %lld", (long long)ds_id[i]);
+        Slot s;
+        s.ds_id = ds_id[i];
+        s.numel = numel[i];
+        s.persistent = numel[i] < persistence_threshold;
+        s.ps = s.persistent ? s.numel : (s.numel + world_size - 1) / world_size;
+        s.offset = offset;
+        offset += s.ps;
+        L->index.emplace(s.ds_id, k);
+        L->params.push_back(s);
+    }
+    L->shard_numel = offset;
+    *out = L.release();
+    return ok();
+}
+
+void zs3_layout_destroy(zs3_layout_t layout) { delete layout; }
+
+zs3_status zs3_layout_info(zs3_layout_t L, int32_t* world_size, int64_t* threshold, int32_t* n_params,
+                           int64_t* shard_numel, int64_t* bytes_per_rank) {
+    if (L == nullptr) return fail(ZS3_EINVAL, "layout is NULL");
+    if (world_size) *world_size = L->world;
+    if (threshold) *threshold = L->threshold;
+    if (n_params) *n_params = static_cast<int32_t>(L->params.size());
+    if (shard_numel) *shard_numel = L->shard_numel;
+    if (bytes_per_rank) *bytes_per_rank = 16 * L->shard_numel;
+    return ok();
+}
+
+static void put_slot(const Slot& s, int64_t* numel, int64_t* ps, int32_t* persistent, int64_t* offset) {
+    if (numel) *numel = s.numel;
+    if (ps) *ps = s.ps;
+    if (persistent) *persistent = s.persistent ? 1 : 0;
+    if (offset) *offset = s.offset;
+}
+
+zs3_status zs3_layout_param_at(zs3_layout_t L, int32_t index, int64_t* ds_id, int64_t* numel, int64_t* ps,
+                               int32_t* persistent, int64_t* offset) {
+    if (L == nullptr) return fail(ZS3_EINVAL, "layout is NULL");
+    if (index < 0 || index >= static_cast<int32_t>(L->params.size())) return fail(ZS3_EINVAL, "index %d out of range", index);
+    const Slot& s = L->params[index];
+    if (ds_id) *ds_id = s.ds_id;
+    put_slot(s, numel, ps, persistent, offset);
+    return ok();
+}
+
+zs3_status zs3_layout_param(zs3_layout_t L, int64_t ds_id, int64_t* numel, int64_t* ps, int32_t* persistent,
+                            int64_t* offset) {
+    if (L == nullptr) return fail(ZS3_EINVAL, "layout is NULL");
+    auto it = L->index.find(ds_id);
+    if (it == L->index.end()) return fail(ZS3_ENOTFOUND, "ds_id %lld is not in the layout", (long long)ds_id);
+    put_slot(L->params[it->second], numel, ps, persistent, offset);
+    return ok();
+}
+
+zs3_status zs3_layout_own_range(zs3_layout_t L, int64_t ds_id, int32_t rank, int64_t* lo, int64_t* hi) {
+    zs3_status s = check_layout_rank(L, rank);
+    if (s != ZS3_OK) return s;
+    auto it = L->index.find(ds_id);
+    if (it == L->index.end()) return fail(ZS3_ENOTFOUND, "ds_id %lld is not in the layout", (long long)ds_id);
+    int64_t a, b;
+    L->params[it->second].own_range(rank, &a, &b);
+    if (lo) *lo = a;
+    if (hi) *hi = b;
+    return ok();
+}
+
+// Greedy bucketing: close the bucket before an item that would take it past
+// `limit`, unless the bucket is empty.
+zs3_status zs3_plan_buckets(zs3_layout_t L, int32_t kind, int64_t limit, int32_t cap, int32_t* n_buckets,
+                            int32_t* starts, int64_t* ds_ids_out) {
+    if (L == nullptr || n_buckets == nullptr) return fail(ZS3_EINVAL, "layout or n_buckets is NULL");
+    if (kind != ZS3_GATHER_BUCKETS && kind != ZS3_REDUCE_BUCKETS) return fail(ZS3_EINVAL, "unknown bucket kind %d", kind);
+    if (limit < 1) return fail(ZS3_EINVAL, "bucket limit < 1");
+    std::vector<const Slot*> items;
+    if (kind == ZS3_GATHER_BUCKETS) {
+        for (const Slot& s : L->params)
+            if (!s.persistent) items.push_back(&s);
+    } else {
+        for (auto it = L->params.rbegin(); it != L->params.rend(); ++it) items.push_back(&*it);
+    }
+    std::vector<int32_t> st;
+    int64_t fill = 0;
+    for (size_t i = 0; i < items.size(); ++i) {
+        if (st.empty() || (fill > 0 && fill + items[i]->numel > limit)) {
+            st.push_back(static_cast<int32_t>(i));
+            fill = 0;
+        }
+        fill += items[i]->numel;
+    }
+    const int32_t nb = static_cast<int32_t>(st.size());
+    *n_buckets = nb;
+    if (cap < nb + 1 || starts == nullptr || (ds_ids_out == nullptr && !items.empty()))
+        return fail(ZS3_EINVAL, "output capacity too small: %d buckets need %d starts", nb, nb + 1);
+    for (int32_t b = 0; b < nb; ++b) starts[b] = st[b];
+    starts[nb] = static_cast<int32_t>(items.size());
+    for (size_t i = 0; i < items.size(); ++i) ds_ids_out[i] = items[i]->ds_id;
+    return ok();
+}
+
+zs3_status zs3_sub_groups(zs3_layout_t L, int64_t sub_group_size, int32_t cap, int32_t* n_groups, int64_t* begin_end) {
+    if (L == nullptr || n_groups == nullptr) return fail(ZS3_EINVAL, "layout or n_groups is NULL");
+    if (sub_group_size < 1) return fail(ZS3_EINVAL, "sub_group_size < 1");
+    std::vector<std::pair<int64_t, int64_t>> groups;
+    int64_t fill = 0;
+    for (const Slot& s : L->params) {
+        if (groups.empty() || (fill > 0 && fill + s.ps > sub_group_size)) {
+            groups.emplace_back(s.offset, s.offset);
+            fill = 0;
+        }
+        groups.back().second = s.offset + s.ps;
+        fill += s.ps;
+    }
+    const int32_t ng = static_cast<int32_t>(groups.size());
+    *n_groups = ng;
+    if (cap < ng || (begin_end == nullptr && ng > 0)) return fail(ZS3_EINVAL, "output capacity too small: %d groups", ng);
+    for (int32_t g = 0; g < ng; ++g) {
+        begin_end[2 * g] = groups[g].first;
+        begin_end[2 * g + 1] = groups[g].second;
+    }
+    return ok();
+}
+
+zs3_status zs3_bucket_sizes(zs3_layout_t L, int32_t n, const int64_t* ds_ids, int64_t* chunk_numel, int64_t* full_numel) {
+    if (L == nullptr) return fail(ZS3_EINVAL, "layout is NULL");
+    std::vector<int32_t> pos, order;
+    zs3_status s = resolve(L, n, ds_ids, false, &pos, &order);
+    if (s != ZS3_OK) return s;
+    int64_t c = 0, f = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        c += L->params[pos[i]].ps;
+        f += L->params[pos[i]].numel;
+    }
+    if (chunk_numel) *chunk_numel = c;
+    if (full_numel) *full_numel = f;
+    return ok();
+}
+
+// ---------------------------------------------------------------- (1)
+
+zs3_status zs3_partition(zs3_layout_t L, int32_t rank, int32_t dtype, int32_t n, const int64_t* ds_ids,
+                         const void* const* full_params, void* shard_flat, void* stream) {
+    zs3_status s = check_layout_rank(L, rank);
+    if (s != ZS3_OK) return s;
+    if ((s = check_dtype(dtype)) != ZS3_OK) return s;
+    std::vector<int32_t> pos, order;
+    if ((s = resolve(L, n, ds_ids, true, &pos, &order)) != ZS3_OK) return s;
+    if (n == 0) return ok();
+    if (full_params == nullptr) return fail(ZS3_EINVAL, "full_params is NULL");
+    if ((s = check_ptr16(shard_flat, "shard_flat")) != ZS3_OK) return s;
+    const int64_t shard_bytes = 2 * L->shard_numel;
+    for (int32_t i = 0; i < n; ++i) {
+        if ((s = check_ptr16(full_params[i], "full_params[i]")) != ZS3_OK) return s;
+        if (overlap(full_params[i], 2 * L->params[pos[i]].numel, shard_flat, shard_bytes))
+            return fail(ZS3_EALIAS, "full_params[%d] overlaps shard_flat", i);
+    }
+    Key key{{kOpPartition, device_id(), rank, n, reinterpret_cast<int64_t>(shard_flat)}};
+    for (int32_t k : order) {
+        key.w.push_back(L->params[pos[k]].ds_id);
+        key.w.push_back(reinterpret_cast<int64_t>(full_params[k]));
+    }
+    Plan* plan = find_plan(L, key);
+    if (plan == nullptr) {
+        std::vector<CopySeg> segs;
+        uint16_t* base = static_cast<uint16_t*>(shard_flat);
+        for (int32_t k : order) {
+            const Slot& p = L->params[pos[k]];
+            int64_t lo, hi;
+            p.own_range(rank, &lo, &hi);
+            const uint16_t* src = static_cast<const uint16_t*>(full_params[k]);
+            segs.push_back(CopySeg{src + lo, base + p.offset, hi - lo, 0});
+            segs.push_back(CopySeg{nullptr, base + p.offset + (hi - lo), p.ps - (hi - lo), 0});
+        }
+        if ((s = build_copy_plan(L, std::move(key), segs, &plan)) != ZS3_OK) return s;
+    }
+    return run_copy(plan, stream);
+}
+
+// ---------------------------------------------------------------- (2)
+
+zs3_status zs3_gather_coalesced(zs3_layout_t L, int32_t rank, int32_t dtype, int32_t mode, int32_t n,
+                                const int64_t* ds_ids, const void* shard_flat, void* own_chunk,
+                                const void* const* rank_chunks, void* full_flat, int64_t* full_offsets,
+                                void* stream) {
+    zs3_status s = check_layout_rank(L, rank);
+    if (s != ZS3_OK) return s;
+    if ((s = check_dtype(dtype)) != ZS3_OK) return s;
+    if (mode < 1 || mode > (ZS3_PACK | ZS3_UNPACK)) return fail(ZS3_EINVAL, "mode %d is not PACK, UNPACK or both", mode);
+    std::vector<int32_t> pos, order;
+    if ((s = resolve(L, n, ds_ids, false, &pos, &order)) != ZS3_OK) return s;
+    const int32_t N = L->world;
+    // chunk offsets c_j and full offsets f_j in ascending ds_id
+    std::vector<int64_t> c(n), f(n);
+    int64_t chunk = 0, full = 0;
+    for (int32_t k : order) {
+        c[k] = chunk;
+        f[k] = full;
+        chunk += L->params[pos[k]].ps;
+        full += L->params[pos[k]].numel;
+    }
+    const bool do_pack = (mode & ZS3_PACK) != 0, do_unpack = (mode & ZS3_UNPACK) != 0;
+    if (do_pack) {
+        if ((s = check_ptr16(shard_flat, "shard_flat")) != ZS3_OK) return s;
+        if ((s = check_ptr16(own_chunk, "own_chunk")) != ZS3_OK) return s;
+        if (overlap(shard_flat, 2 * L->shard_numel, own_chunk, 2 * chunk))
+            return fail(ZS3_EALIAS, "own_chunk overlaps shard_flat");
+    }
+    if (do_unpack) {
+        if (rank_chunks == nullptr) return fail(ZS3_EINVAL, "rank_chunks is NULL");
+        if ((s = check_ptr16(full_flat, "full_flat")) != ZS3_OK) return s;
+        for (int32_t v = 0; v < N; ++v) {
+            if ((s = check_ptr16(rank_chunks[v], "rank_chunks[v]")) != ZS3_OK) return s;
+            if (overlap(rank_chunks[v], 2 * chunk, full_flat, 2 * full))
+                return fail(ZS3_EALIAS, "rank_chunks[%d] overlaps full_flat", v);
+        }
+        if (do_pack && overlap(own_chunk, 2 * chunk, full_flat, 2 * full))
+            return fail(ZS3_EALIAS, "own_chunk overlaps full_flat");
+    }
+    if (full_offsets != nullptr)
+        for (int32_t i = 0; i < n; ++i) full_offsets[i] = f[i];
+    if (n == 0) return ok();
+
+    if (do_pack) {
+        Key key{{kOpPack, device_id(), rank, reinterpret_cast<int64_t>(shard_flat), reinterpret_cast<int64_t>(own_chunk)}};
+        for (int32_t k : order) key.w.push_back(L->params[pos[k]].ds_id);
+        Plan* plan = find_plan(L, key);
+        if (plan == nullptr) {
+            std::vector<CopySeg> segs;
+            const uint16_t* src = static_cast<const uint16_t*>(shard_flat);
+            uint16_t* dst = static_cast<uint16_t*>(own_chunk);
+            for (int32_t k : order) {
+                const Slot& p = L->params[pos[k]];
+                segs.push_back(CopySeg{src + p.offset, dst + c[k], p.ps, 0});
+            }
+            if ((s = build_copy_plan(L, std::move(key), segs, &plan)) != ZS3_OK) return s;
+        }
+        if ((s = run_copy(plan, stream)) != ZS3_OK) return s;
+    }
+    if (do_unpack) {
+        Key key{{kOpUnpack, device_id(), reinterpret_cast<int64_t>(full_flat)}};
+        for (int32_t v = 0; v < N; ++v) key.w.push_back(reinterpret_cast<int64_t>(rank_chunks[v]));
+        for (int32_t k : order) key.w.push_back(L->params[pos[k]].ds_id);
+        Plan* plan = find_plan(L, key);
+        if (plan == nullptr) {
+            std::vector<CopySeg> segs;
+            uint16_t* dst = static_cast<uint16_t*>(full_flat);
+            for (int32_t k : order) {
+                const Slot& p = L->params[pos[k]];
+                for (int32_t v = 0; v < N; ++v) {
+                    int64_t lo, hi;
+                    p.own_range(v, &lo, &hi);
+                    const uint16_t* src = static_cast<const uint16_t*>(rank_chunks[v]) + c[k];
+                    segs.push_back(CopySeg{src, dst + f[k] + lo, hi - lo, 0});
+                }
+            }
+            if ((s = build_copy_plan(L, std::move(key), segs, &plan)) != ZS3_OK) return s;
+        }
+        if ((s = run_copy(plan, stream)) != ZS3_OK) return s;
+    }
+    return ok();
+}
+
+// ---------------------------------------------------------------- (3)
+
+zs3_status zs3_reduce_scatter_local(zs3_layout_t L, int32_t rank, int32_t dtype, int32_t n, const int64_t* ds_ids,
+                                    const void* const* src, void* grad_flat, void* stream) {
+    zs3_status s = check_layout_rank(L, rank);
+    if (s != ZS3_OK) return s;
+    if ((s = check_dtype(dtype)) != ZS3_OK) return s;
+    std::vector<int32_t> pos, order;
+    if ((s = resolve(L, n, ds_ids, true, &pos, &order)) != ZS3_OK) return s;
+    if (n == 0) return ok();
+    if (src == nullptr) return fail(ZS3_EINVAL, "src is NULL");
+    if ((s = check_ptr16(grad_flat, "grad_flat")) != ZS3_OK) return s;
+    const int32_t N = L->world;
+    uint16_t* gbase = static_cast<uint16_t*>(grad_flat);
+    for (int32_t i = 0; i < n; ++i) {
+        const Slot& p = L->params[pos[i]];
+        const int64_t real = p.real(rank);
+        for (int32_t v = 0; v < N; ++v) {
+            const void* q = src[static_cast<int64_t>(i) * N + v];
+            if (real == 0) continue;
+            if ((s = check_ptr16(q, "src[i*N+v]")) != ZS3_OK) return s;
+            for (int32_t j = 0; j < n; ++j) {
+                const Slot& o = L->params[pos[j]];
+                if (overlap(q, 2 * real, gbase + o.offset, 2 * o.ps))
+                    return fail(ZS3_EALIAS, "src[%d*N+%d] overlaps the written part of grad_flat", i, v);
+            }
+        }
+    }
+    Key key{{kOpReduce, device_id(), rank, reinterpret_cast<int64_t>(grad_flat)}};
+    for (int32_t k : order) {
+        key.w.push_back(L->params[pos[k]].ds_id);
+        for (int32_t v = 0; v < N; ++v) key.w.push_back(reinterpret_cast<int64_t>(src[static_cast<int64_t>(k) * N + v]));
+    }
+    Plan* plan = find_plan(L, key);
+    if (plan == nullptr) {
+        std::vector<RsSeg> segs;
+        std::vector<const uint16_t*> srcs;
+        std::vector<Piece> pieces;
+        bool co = true;
+        for (int32_t k : order) {
+            const Slot& p = L->params[pos[k]];
+            const int64_t real = p.real(rank);
+            uint16_t* dst = gbase + p.offset;
+            const int32_t si = static_cast<int32_t>(segs.size());
+            segs.push_back(RsSeg{dst, real, p.ps, static_cast<int64_t>(srcs.size())});
+            for (int32_t v = 0; v < N; ++v) {
+                const uint16_t* q = static_cast<const uint16_t*>(src[static_cast<int64_t>(k) * N + v]);
+                if (real == 0) q = nullptr;
+                srcs.push_back(q);
+                if (q != nullptr && ((reinterpret_cast<uintptr_t>(q) ^ reinterpret_cast<uintptr_t>(dst)) & 15u) != 0) co = false;
+            }
+            add_pieces(&pieces, si, reinterpret_cast<uintptr_t>(dst), p.ps, kRsPiece);
+        }
+        if ((s = check_grid(static_cast<int64_t>(pieces.size()))) != ZS3_OK) return s;
+        Plan np;
+        np.n_pieces = static_cast<int64_t>(pieces.size());
+        np.co_aligned = co;
+        std::vector<size_t> offs;
+        s = upload(&np,
+                   {{segs.data(), segs.size() * sizeof(RsSeg)},
+                    {pieces.data(), pieces.size() * sizeof(Piece)},
+                    {srcs.data(), srcs.size() * sizeof(const uint16_t*)}},
+                   0, &offs);
+        if (s != ZS3_OK) return s;
+        np.off_segs = offs[0];
+        np.off_pieces = offs[1];
+        np.off_srcs = offs[2];
+        store_plan(L, std::move(key), std::move(np), &plan);
+    }
+    return hip_status(launch_reduce_scatter(dtype, plan->at<RsSeg>(plan->off_segs), plan->at<Piece>(plan->off_pieces),
+                                            plan->n_pieces, plan->at<const uint16_t*>(plan->off_srcs), N,
+                                            plan->co_aligned, static_cast<hipStream_t>(stream)),
+                      "reduce-scatter kernel launch");
+}
+
+// ---------------------------------------------------------------- (4)
+
+zs3_status zs3_grad_norm(zs3_layout_t L, int32_t rank, int32_t dtype, const void* grad_flat, double* sumsq,
+                         int32_t finalize, double max_norm, double loss_scale, double* norm_out, float* scale_out,
+                         int32_t* nonfinite, void* stream) {
+    zs3_status s = check_layout_rank(L, rank);
+    if (s != ZS3_OK) return s;
+    if ((s = check_dtype(dtype)) != ZS3_OK) return s;
+    if ((s = check_ptr16(grad_flat, "grad_flat")) != ZS3_OK) return s;
+    if (sumsq == nullptr || !aligned(sumsq, 8)) return fail(ZS3_EINVAL, "sumsq is NULL or not 8-byte aligned");
+    if (finalize) {
+        if (norm_out == nullptr || scale_out == nullptr || nonfinite == nullptr)
+            return fail(ZS3_EINVAL, "finalize needs norm_out, scale_out and nonfinite");
+        if (!aligned(norm_out, 8) || !aligned(scale_out, 4) || !aligned(nonfinite, 4))
+            return fail(ZS3_EINVAL, "misaligned norm_out, scale_out or nonfinite");
+        if (!(max_norm > 0.0) || !(loss_scale > 0.0)) return fail(ZS3_EINVAL, "max_norm and loss_scale must be > 0");
+    }
+    if (overlap(sumsq, 8 * (L->world + 1), grad_flat, 2 * L->shard_numel))
+        return fail(ZS3_EALIAS, "sumsq overlaps grad_flat");
+    Key key{{kOpNorm, device_id(), rank, reinterpret_cast<int64_t>(grad_flat)}};
+    Plan* plan = find_plan(L, key);
+    if (plan == nullptr) {
+        // real runs: partitioned first, then persistent; adjacent runs merged
+        std::vector<std::pair<int64_t, int64_t>> part, pers;
+        for (const Slot& p : L->params) {
+            auto& runs = p.persistent ? pers : part;
+            const int64_t real = p.real(rank);
+            if (real == 0) continue;
+            if (!runs.empty() && runs.back().first + runs.back().second == p.offset) runs.back().second += real;
+            else runs.emplace_back(p.offset, real);
+        }
+        const uintptr_t base = reinterpret_cast<uintptr_t>(grad_flat);
+        std::vector<Span> spans;
+        for (auto& r : part) add_spans(&spans, r.first, r.second, ((16u - ((base + 2 * r.first) & 15u)) & 15u) >> 1, kNormPiece);
+        const int64_t n_part = static_cast<int64_t>(spans.size());
+        for (auto& r : pers) add_spans(&spans, r.first, r.second, ((16u - ((base + 2 * r.first) & 15u)) & 15u) >> 1, kNormPiece);
+        if ((s = check_grid(static_cast<int64_t>(spans.size()))) != ZS3_OK) return s;
+        Plan np;
+        np.n_pieces = static_cast<int64_t>(spans.size());
+        np.n_part = n_part;
+        std::vector<size_t> offs;
+        s = upload(&np, {{spans.data(), spans.size() * sizeof(Span)}}, std::max<size_t>(8, spans.size() * sizeof(double)), &offs);
+        if (s != ZS3_OK) return s;
+        np.off_pieces = offs[0];
+        store_plan(L, std::move(key), std::move(np), &plan);
+    }
+    return hip_status(launch_grad_norm(dtype, static_cast<const uint16_t*>(grad_flat), plan->at<Span>(plan->off_pieces),
+                                       plan->n_pieces, plan->n_part, plan->at<double>(plan->off_scratch), sumsq, rank,
+                                       L->world, finalize, max_norm, loss_scale, norm_out, scale_out, nonfinite,
+                                       static_cast<hipStream_t>(stream)),
+                      "grad-norm kernel launch");
+}
+
+// ---------------------------------------------------------------- (5)
+
+zs3_status zs3_adam_step(zs3_layout_t L, int32_t rank, int32_t dtype, int64_t begin, int64_t end, float* master,
+                         float* exp_avg, float* exp_avg_sq, const void* grad_flat, void* shard_flat,
+                         const float* scale, const int32_t* nonfinite, const zs3_adam_params* hp, void* stream) {
+    zs3_status s = check_layout_rank(L, rank);
+    if (s != ZS3_OK) return s;
+    if ((s = check_dtype(dtype)) != ZS3_OK) return s;
+    if (hp == nullptr) return fail(ZS3_EINVAL, "hp is NULL");
+    if (hp->step < 1) return fail(ZS3_EINVAL, "step %lld < 1", (long long)hp->step);
+    if (begin < 0 || end < begin || end > L->shard_numel)
+        return fail(ZS3_EINVAL, "range [%lld, %lld) outside [0, %lld]", (long long)begin, (long long)end,
+                    (long long)L->shard_numel);
+    if (master == nullptr || exp_avg == nullptr || exp_avg_sq == nullptr || scale == nullptr)
+        return fail(ZS3_EINVAL, "master, exp_avg, exp_avg_sq or scale is NULL");
+    if (!aligned(master, 4) || !aligned(exp_avg, 4) || !aligned(exp_avg_sq, 4) || !aligned(scale, 4) ||
+        (nonfinite != nullptr && !aligned(nonfinite, 4)))
+        return fail(ZS3_EINVAL, "fp32 or int32 pointer not 4-byte aligned");
+    if ((s = check_ptr16(grad_flat, "grad_flat")) != ZS3_OK) return s;
+    if ((s = check_ptr16(shard_flat, "shard_flat")) != ZS3_OK) return s;
+    const int64_t nb = end - begin;
+    const void* arr[5] = {master + begin, exp_avg + begin, exp_avg_sq + begin,
+                          static_cast<const uint16_t*>(grad_flat) + begin, static_cast<uint16_t*>(shard_flat) + begin};
+    const int64_t bytes[5] = {4 * nb, 4 * nb, 4 * nb, 2 * nb, 2 * nb};
+    for (int i = 0; i < 5; ++i)
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(arr[i], bytes[i], arr[j], bytes[j])) return fail(ZS3_EALIAS, "Adam arrays %d and %d overlap", i, j);
+    if (nb == 0) return ok();
+
+    AdamConsts c;
+    const double t = static_cast<double>(hp->step);
+    c.lr = static_cast<float>(hp->lr);
+    c.b1 = static_cast<float>(hp->beta1);
+    c.b2 = static_cast<float>(hp->beta2);
+    c.omb1 = static_cast<float>(1.0 - hp->beta1);
+    c.omb2 = static_cast<float>(1.0 - hp->beta2);
+    c.bc1 = static_cast<float>(1.0 - std::pow(hp->beta1, t));
+    c.bc2 = static_cast<float>(1.0 - std::pow(hp->beta2, t));
+    c.eps = static_cast<float>(hp->eps);
+    c.lrwd = static_cast<float>(hp->lr * hp->weight_decay);
+    c.has_wd = hp->weight_decay != 0.0 ? 1 : 0;
+
+    const bool vec_ok = aligned(master, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16) &&
+                        aligned(grad_flat, 16) && aligned(shard_flat, 16);
+    Key key{{kOpAdam, device_id(), rank, begin, end}};
+    Plan* plan = find_plan(L, key);
+    if (plan == nullptr) {
+        // real runs of [begin, end): padding positions are skipped
+        std::vector<std::pair<int64_t, int64_t>> runs;
+        for (const Slot& p : L->params) {
+            const int64_t a = std::max(begin, p.offset);
+            const int64_t b = std::min(end, p.offset + p.real(rank));
+            if (b <= a) continue;
+            if (!runs.empty() && runs.back().first + runs.back().second == a) runs.back().second += b - a;
+            else runs.emplace_back(a, b - a);
+        }
+        std::vector<Span> spans;
+        for (auto& r : runs) add_spans(&spans, r.first, r.second, (8 - (r.first & 7)) & 7, kAdamPiece);
+        if ((s = check_grid(static_cast<int64_t>(spans.size()))) != ZS3_OK) return s;
+        Plan np;
+        np.n_pieces = static_cast<int64_t>(spans.size());
+        std::vector<size_t> offs;
+        s = upload(&np, {{spans.data(), spans.size() * sizeof(Span)}}, 0, &offs);
+        if (s != ZS3_OK) return s;
+        np.off_pieces = offs[0];
+        store_plan(L, std::move(key), std::move(np), &plan);
+    }
+    return hip_status(launch_adam(dtype, plan->at<Span>(plan->off_pieces), plan->n_pieces, master, exp_avg, exp_avg_sq,
+                                  static_cast<const uint16_t*>(grad_flat), static_cast<uint16_t*>(shard_flat), scale,
+                                  nonfinite, c, vec_ok, static_cast<hipStream_t>(stream)),
+                      "Adam kernel launch");
+}
+
+}  // extern "C"
