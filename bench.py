@@ -1,0 +1,331 @@
+"""Benchmark of the fused ZeRO-3 shard step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c4] [--rank R]
+
+A step is one pass of the whole hot path for one rank: forward and
+backward coalesced all-gather of every gather bucket (pack + unpack), the
+reduce-scatter of every gradient bucket, the pre-step re-partition, the
+global gradient norm, and the fused Adam + cast of every sub-group.  The N
+data-parallel ranks are N virtual ranks in this GPU's HBM; inputs are
+synthetic (seeded N(0, 0.02) weights, N(0, 1e-3) gradients with 1% x100
+outliers) and resident in HBM before timing starts.
+
+Prints ONE JSON line: effective HBM GB/s of the step (algorithmic bytes /
+time), its fraction of 8 TB/s and params/s, the roofline entry of the
+dominant kernel (unpack) timed with HIP events on the launch stream, and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective HBM GB/s (% of 8 TB/s) and params/s for fused ZeRO-3 shard step"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c4")
+    ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=12, help="decoder layers in the oracle's sample")
+    ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
+                    help="also run a plain device copy of this many GiB (counter calibration)")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "api.cpp", "zs3_internal.hpp"):
+        with open(os.path.join(ROOT, "zero_sharded_state_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_entry(config: str):
+    """HBM bytes per unpack launch from the committed counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"unpack_traffic_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_digest") != source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def make_step(cfg, rank):
+    from zero_sharded_state_amd.shard_step import AdamConfig, ShardStep
+
+    return ShardStep(world_size=cfg.world_size, rank=rank, threshold=cfg.threshold, ds_ids=cfg.ds_ids,
+                     numels=cfg.numels, dtype=cfg.dtype, prefetch_bucket_size=cfg.prefetch_bucket_size,
+                     reduce_bucket_size=cfg.reduce_bucket_size, sub_group_size=cfg.sub_group_size,
+                     adam=AdamConfig(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay),
+                     max_norm=cfg.max_norm)
+
+
+def fill_inputs(step, cfg):
+    from synth.gen import KIND_GRAD, KIND_WEIGHT, device_normal16
+
+    dev = step.device
+    if step.F:
+        device_normal16(step.F, cfg.weight_std, cfg.dtype, dev, (cfg.seed, cfg.config_id, KIND_WEIGHT, 0),
+                        out=step.full)
+    if step.P:
+        device_normal16(step.P, cfg.weight_std, cfg.dtype, dev, (cfg.seed, cfg.config_id, KIND_WEIGHT, 1),
+                        out=step.pers_full)
+    device_normal16(step.N * step.S, cfg.grad_std, cfg.dtype, dev, (cfg.seed, cfg.config_id, KIND_GRAD, step.rank),
+                    outlier_prob=cfg.outlier_prob, outlier_mult=cfg.outlier_mult, out=step.recv)
+    step.init_from_full()
+    step.reduce_scatter()
+    step.fill_peer_norms()
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# --------------------------------------------------------------------------
+
+def cpu_baseline(step, cfg, layers: int):
+    import numpy as np
+
+    import oracle
+
+    # the sample: the parameters of the first `layers` decoder layers (every
+    # ds_id whose name carries a layer index < layers), same N, rank, dtype
+    def layer_of(name):
+        for tok in name.split("."):
+            if tok.isdigit():
+                return int(tok)
+        return None
+
+    ids = [d for d, p in enumerate(cfg.params) if layer_of(p.name) is not None and layer_of(p.name) < layers]
+    if not ids:
+        ids = list(range(min(4, len(cfg.params))))
+    numels = [cfg.params[d].numel for d in ids]
+    N, r, dt = step.N, step.rank, cfg.dtype
+    L = oracle.make_layout(N, cfg.threshold, ids, numels)
+    idset = set(ids)
+
+    def h16(t):
+        return t.cpu().numpy().view(np.uint16)
+
+    full = {}
+    for d in ids:
+        p = step.by_id[d]
+        if p["persistent"]:
+            o = step.pers_off[d]
+            full[d] = h16(step.pers_full[o:o + p["numel"]])
+        else:
+            o = step.full_off[d]
+            full[d] = h16(step.full[o:o + p["numel"]])
+    buckets = [b for b in step.gather_buckets if set(b) <= idset]
+    chunks = {}
+    for bi, b in enumerate(step.gather_buckets):
+        if set(b) <= idset:
+            _, _, w, c = step.bucket_meta[bi]
+            chunks[tuple(b)] = [h16(step.wire[w + v * c:w + (v + 1) * c]) for v in range(N)]
+    grads = []
+    for v in range(N):
+        g = {}
+        for d in ids:
+            p = step.by_id[d]
+            lo, hi = p["own"]
+            a = np.zeros(p["numel"], np.uint16)
+            o = v * step.S + p["shard_offset"]
+            a[lo:hi] = h16(step.recv[o:o + (hi - lo)])
+            g[d] = a
+        grads.append(g)
+    shard = oracle.partition(L, r, full)
+    master, m, v_ = oracle.init_state(shard, dt)
+    grad_flat = np.zeros(L.shard_numel, np.uint16)
+    hp = oracle.AdamHParams(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, 1)
+
+    t0 = time.perf_counter()
+    for _ in range(2):                                       # forward + backward all-gather
+        for b in buckets:
+            oracle.pack(L, r, b, shard)
+            oracle.unpack(L, b, chunks[tuple(b)])
+    oracle.reduce_scatter(L, r, dt, ids[::-1], grads, grad_flat)
+    shard = oracle.partition(L, r, full)
+    a, q = oracle.grad_norm_partial(L, r, dt, grad_flat)
+    norm, coef, scale, bad = oracle.grad_norm_finalize([a] * N, q, cfg.max_norm)
+    oracle.adam_step(L, r, dt, 0, L.shard_numel, master, m, v_, grad_flat, shard, scale, bad, hp)
+    secs = time.perf_counter() - t0
+
+    part_real = sum(L.own_range(p, r)[1] - L.own_range(p, r)[0] for p in L.params if not p.persistent)
+    own = sum(L.own_range(p, r)[1] - L.own_range(p, r)[0] for p in L.params)
+    F = sum(sum(L.slot(d).numel for d in b) for b in buckets)
+    nbytes = 2 * 4 * part_real + 2 * 4 * F + (2 * N * own + 2 * own) + 4 * own + 2 * own + 28 * own
+    return {
+        "value": round(nbytes / secs / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{layers} decoder layer(s) of the same workload ({len(ids)} params, {sum(numels):,} elements, "
+                   f"{own:,} own elements of rank {r}), one whole step, numpy single-threaded; "
+                   f"{nbytes / 1e9:.3f} GB algorithmic in {secs:.2f} s"),
+        "params_per_s": round(own / secs, 1),
+        "host_cores_available": len(os.sched_getaffinity(0)),
+    }
+
+
+# --------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the N data-parallel ranks are virtual "
+                                   "ranks in one GPU's HBM; --gpus must be 1", "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+
+    from synth import get_config
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    cfg = get_config(args.config)
+    rank = cfg.bench_rank if args.rank is None else args.rank
+    log(f"config {cfg.name}: {cfg.title}, rank {rank}")
+    step = make_step(cfg, rank)
+    log(f"layout: S+P={step.S:,} own real={step.own_real:,} F={step.F:,} gather buckets={len(step.gather_buckets)} "
+        f"reduce buckets={len(step.reduce_buckets)} sub-groups={len(step.sub_groups)}")
+    t0 = time.time()
+    fill_inputs(step, cfg)
+    torch.cuda.synchronize()
+    log(f"inputs resident in HBM ({torch.cuda.memory_allocated() / 2**30:.1f} GiB) in {time.time() - t0:.1f} s")
+
+    for _ in range(args.warmup):
+        step.step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    phase_events = []
+    unpack_events = []
+    stream = torch.cuda.current_stream()
+
+    def on_phase(name):
+        e = ev()
+        e.record(stream)
+        phase_events[-1].append((name, e))
+
+    def on_unpack(start):
+        e = ev()
+        e.record(stream)
+        if start:
+            unpack_events.append([e, None])
+        else:
+            unpack_events[-1][1] = e
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        phase_events.append([])
+        step.step(on_phase=on_phase, on_unpack=None if args.no_kernel_events else on_unpack)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    log(f"timed {args.steps} steps in {wall:.3f} s")
+
+    ms_per_step = wall * 1e3 / args.steps
+    nbytes = step.algorithmic_bytes()
+    total_bytes = sum(nbytes.values())
+    gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
+    params_per_s = step.own_real / (ms_per_step * 1e-3)
+
+    # per-phase times (HIP events on the launch stream)
+    phases = {}
+    for evs in phase_events:
+        for (name, e0), (_, e1) in zip(evs, evs[1:]):
+            phases[name] = phases.get(name, 0.0) + e0.elapsed_time(e1)
+    phase_bytes = {"gather_fwd": (nbytes["pack"] + nbytes["unpack"]) // 2,
+                   "gather_bwd": (nbytes["pack"] + nbytes["unpack"]) // 2,
+                   "reduce_scatter": nbytes["reduce_scatter"], "partition": nbytes["partition"],
+                   "grad_norm": nbytes["grad_norm"], "adam": nbytes["adam"]}
+    kernels = {}
+    for name, ms in phases.items():
+        ms /= args.steps
+        kernels[name] = {"ms": round(ms, 4), "bytes": phase_bytes[name],
+                         "GBps": round(phase_bytes[name] / (ms * 1e-3) / 1e9, 1)}
+
+    roofline = None
+    if unpack_events:
+        durs = [a.elapsed_time(b) for a, b in unpack_events]
+        per_launch_bytes = nbytes["unpack"] / (2 * len(step.gather_buckets))
+        avg_ms = sum(durs) / len(durs)
+        achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
+        traffic = traffic_entry(cfg.name)
+        roofline = {"kernel": "unpack (k_copy<3>)", "bound": "hbm", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic, "launches": len(durs), "avg_launch_ms": round(avg_ms, 5),
+                    "algorithmic_bytes_per_launch": int(per_launch_bytes)}
+
+    if args.calibrate_copy_gib > 0:
+        n = int(args.calibrate_copy_gib * 2**30) // 2
+        a = torch.empty(n, dtype=torch.int16, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("running the CPU oracle on its sample")
+        cpu = cpu_baseline(step, cfg, args.cpu_layers)
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "params_per_s": round(params_per_s, 1),
+        "bytes_per_step": total_bytes,
+        "config": {
+            "workload": f"{cfg.title}: fused shard step of rank {rank} ({cfg.total_params:,} params, "
+                        f"{step.own_real:,} own elements)",
+            "name": cfg.name, "world_size": cfg.world_size, "rank": rank, "storage_dtype": cfg.dtype,
+            "params": cfg.total_params, "own_elements": step.own_real,
+            "gather_buckets": len(step.gather_buckets), "reduce_buckets": len(step.reduce_buckets),
+            "sub_groups": len(step.sub_groups), "prefetch_bucket_size": cfg.prefetch_bucket_size,
+            "reduce_bucket_size": cfg.reduce_bucket_size, "sub_group_size": cfg.sub_group_size,
+        },
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "source_digest": source_digest(),
+    }
+    print(json.dumps(line), flush=True)
+    step.destroy()
+
+
+if __name__ == "__main__":
+    main()

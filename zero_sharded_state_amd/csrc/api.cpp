@@ -293,8 +293,8 @@ zs3_status build_copy_plan(zs3_layout* L, Key&& key, const std::vector<CopySeg>&
     return store_plan(L, std::move(key), std::move(plan), out);
 }
 
-zs3_status run_copy(const Plan* p, void* stream) {
-    return hip_status(launch_copy(p->at<CopySeg>(p->off_segs), p->at<Piece>(p->off_pieces), p->n_pieces,
+zs3_status run_copy(CopyKind kind, const Plan* p, void* stream) {
+    return hip_status(launch_copy(kind, p->at<CopySeg>(p->off_segs), p->at<Piece>(p->off_pieces), p->n_pieces,
                                   static_cast<hipStream_t>(stream)),
                       "copy kernel launch");
 }
@@ -529,7 +529,7 @@ zs3_status zs3_partition(zs3_layout_t L, int32_t rank, int32_t dtype, int32_t n,
         }
         if ((s = build_copy_plan(L, std::move(key), segs, &plan)) != ZS3_OK) return s;
     }
-    return run_copy(plan, stream);
+    return run_copy(kCopyPartition, plan, stream);
 }
 
 // ---------------------------------------------------------------- (2)
@@ -590,7 +590,7 @@ zs3_status zs3_gather_coalesced(zs3_layout_t L, int32_t rank, int32_t dtype, int
             }
             if ((s = build_copy_plan(L, std::move(key), segs, &plan)) != ZS3_OK) return s;
         }
-        if ((s = run_copy(plan, stream)) != ZS3_OK) return s;
+        if ((s = run_copy(kCopyPack, plan, stream)) != ZS3_OK) return s;
     }
     if (do_unpack) {
         Key key{{kOpUnpack, device_id(), reinterpret_cast<int64_t>(full_flat)}};
@@ -611,7 +611,7 @@ zs3_status zs3_gather_coalesced(zs3_layout_t L, int32_t rank, int32_t dtype, int
             }
             if ((s = build_copy_plan(L, std::move(key), segs, &plan)) != ZS3_OK) return s;
         }
-        if ((s = run_copy(plan, stream)) != ZS3_OK) return s;
+        if ((s = run_copy(kCopyUnpack, plan, stream)) != ZS3_OK) return s;
     }
     return ok();
 }

@@ -131,6 +131,9 @@ __device__ __forceinline__ void copy_body(const uint16_t* src, uint4* dst, int64
     }
 }
 
+// One body, three kernel names (partition, pack, unpack) so that profiles
+// attribute time to each step of the method.
+template <int OP>
 __global__ __launch_bounds__(kBlock) void k_copy(const CopySeg* __restrict__ segs,
                                                  const Piece* __restrict__ pieces) {
     const Piece pc = pieces[blockIdx.x];
@@ -494,9 +497,15 @@ inline dim3 grid_of(int64_t n) { return dim3(static_cast<uint32_t>(n)); }
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_copy(const CopySeg* segs, const Piece* pieces, int64_t n_pieces, hipStream_t stream) {
+hipError_t launch_copy(CopyKind kind, const CopySeg* segs, const Piece* pieces, int64_t n_pieces,
+                       hipStream_t stream) {
     if (n_pieces <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_copy, grid_of(n_pieces), dim3(kBlock), 0, stream, segs, pieces);
+    const dim3 g = grid_of(n_pieces), b(kBlock);
+    switch (kind) {
+        case kCopyPartition: hipLaunchKernelGGL(k_copy<kCopyPartition>, g, b, 0, stream, segs, pieces); break;
+        case kCopyPack: hipLaunchKernelGGL(k_copy<kCopyPack>, g, b, 0, stream, segs, pieces); break;
+        default: hipLaunchKernelGGL(k_copy<kCopyUnpack>, g, b, 0, stream, segs, pieces); break;
+    }
     return hipGetLastError();
 }
 

@@ -62,8 +62,10 @@ struct AdamConsts {
 
 enum DType : int32_t { kFP16 = 1, kBF16 = 2 };
 
+enum CopyKind : int32_t { kCopyPartition = 1, kCopyPack = 2, kCopyUnpack = 3 };
+
 // ---- launchers (kernels.hip) -------------------------------------------
-hipError_t launch_copy(const CopySeg* segs, const Piece* pieces, int64_t n_pieces,
+hipError_t launch_copy(CopyKind kind, const CopySeg* segs, const Piece* pieces, int64_t n_pieces,
                        hipStream_t stream);
 
 hipError_t launch_reduce_scatter(int32_t dtype, const RsSeg* segs, const Piece* pieces,

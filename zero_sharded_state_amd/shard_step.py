@@ -1,0 +1,277 @@
+"""One rank's ZeRO-3 shard step, with the N data-parallel ranks held as N
+virtual ranks in one GPU's HBM.
+
+The step issues, on one stream, the calls a real rank makes around its
+collectives, in the order the pages give ([llmnex] section 2, [codex]
+5.2, 6.2, 6.3):
+
+1. forward all-gather of every gather bucket: pack the own shard into the
+   rank's chunk of the bucket's wire buffer, then unpack the N chunks into
+   the bucket's full parameters (the other chunks stand for what the
+   collective delivers);
+2. backward all-gather: the same again (parameters were released after the
+   forward);
+3. reduce-scatter of every gradient bucket (backward order) into the flat
+   gradient buffer, from the slices the N ranks send to this rank;
+4. the pre-step pass that puts every parameter back in partitioned form
+   ([codex] 6.3): the own range of each gathered parameter is copied into
+   the flat shard (it already holds those values, so the shard is
+   unchanged);
+5. the global gradient norm and clip scale ([llmnex] pitfall 1);
+6. fused Adam + cast per sub-group.
+
+No call synchronises; nothing is copied to the host.  All buffers are torch
+tensors owned by this object; all arithmetic runs in libzs3's kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Dict, List, Sequence, Tuple
+
+import zero_sharded_state_amd as zs
+
+
+@dataclass
+class AdamConfig:
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.0
+
+
+class ShardStep:
+    def __init__(self, *, world_size: int, rank: int, threshold: int, ds_ids: Sequence[int],
+                 numels: Sequence[int], dtype: str, prefetch_bucket_size: int, reduce_bucket_size: int,
+                 sub_group_size: int, adam: AdamConfig = AdamConfig(), max_norm: float = 1.0,
+                 device: str = "cuda"):
+        import torch
+
+        self.torch = torch
+        self.N, self.rank, self.dtype = int(world_size), int(rank), dtype
+        self.dcode = zs.DTYPES[dtype]
+        self.adam, self.max_norm = adam, float(max_norm)
+        self.device = torch.device(device)
+        self.h = zs.zs3_layout_create(world_size, threshold, ds_ids, numels)
+        info = zs.zs3_layout_info(self.h)
+        self.S = info["shard_numel"]
+        self.params = [zs.zs3_layout_param_at(self.h, i) for i in range(info["n_params"])]
+        self.by_id = {p["ds_id"]: p for p in self.params}
+        for p in self.params:
+            p["own"] = zs.zs3_layout_own_range(self.h, p["ds_id"], self.rank)
+        self.gather_buckets = zs.zs3_plan_buckets(self.h, zs.ZS3_GATHER_BUCKETS, prefetch_bucket_size)
+        self.reduce_buckets = zs.zs3_plan_buckets(self.h, zs.ZS3_REDUCE_BUCKETS, reduce_bucket_size)
+        self.sub_groups = zs.zs3_sub_groups(self.h, sub_group_size)
+
+        # ---- buffer layout (element offsets) ----
+        self.full_off: Dict[int, int] = {}     # ds_id -> offset of its gathered view in `full`
+        self.bucket_meta: List[Tuple[int, int, int, int]] = []   # (full_off, full_n, wire_off, chunk_n)
+        f = w = 0
+        for b in self.gather_buckets:
+            chunk_n, full_n = zs.zs3_bucket_sizes(self.h, b)
+            self.bucket_meta.append((f, full_n, w, chunk_n))
+            o = f
+            for d in b:                         # ds_id order inside a bucket
+                self.full_off[d] = o
+                o += self.by_id[d]["numel"]
+            f += full_n
+            w += self.N * chunk_n
+        self.F, self.W = f, w
+        self.pers = [p for p in self.params if p["persistent"]]
+        self.pers_off = {}
+        o = 0
+        for p in self.pers:
+            self.pers_off[p["ds_id"]] = o
+            o += p["numel"]
+        self.P = o
+        self.own_real = sum(p["own"][1] - p["own"][0] for p in self.params)     # S_real + P
+
+        i16, f32 = torch.int16, torch.float32
+        dev = self.device
+        self.full = torch.empty(max(1, self.F), dtype=i16, device=dev)        # gathered parameters
+        self.pers_full = torch.empty(max(1, self.P), dtype=i16, device=dev)   # whole persistent params
+        self.wire = torch.empty(max(1, self.W), dtype=i16, device=dev)        # per-bucket all-gather output
+        self.shard = torch.zeros(max(1, self.S), dtype=i16, device=dev)
+        self.grad = torch.zeros(max(1, self.S), dtype=i16, device=dev)
+        self.recv = torch.zeros(max(1, self.N * self.S), dtype=i16, device=dev)  # slices sent to this rank
+        self.master = torch.zeros(max(1, self.S), dtype=f32, device=dev)
+        self.exp_avg = torch.zeros_like(self.master)
+        self.exp_avg_sq = torch.zeros_like(self.master)
+        self.sumsq = torch.zeros(self.N + 1, dtype=torch.float64, device=dev)
+        self.outs = torch.zeros(2, dtype=torch.float64, device=dev)   # norm | scale (f32), flag (i32)
+        self.t = 0
+        self._marshal()
+
+    # ------------------------------------------------------------ pointers
+    def full_param_ptr(self, ds_id: int) -> int:
+        p = self.by_id[ds_id]
+        if p["persistent"]:
+            return self.pers_full.data_ptr() + 2 * self.pers_off[ds_id]
+        return self.full.data_ptr() + 2 * self.full_off[ds_id]
+
+    def chunk_ptr(self, bucket: int, v: int) -> int:
+        _, _, w, c = self.bucket_meta[bucket]
+        return self.wire.data_ptr() + 2 * (w + v * c)
+
+    def recv_ptr(self, v: int, ds_id: int) -> int:
+        """Where virtual rank v's slice of parameter ds_id for this rank lives."""
+        return self.recv.data_ptr() + 2 * (v * self.S + self.by_id[ds_id]["shard_offset"])
+
+    @property
+    def norm_ptr(self) -> int:
+        return self.outs.data_ptr()
+
+    @property
+    def scale_ptr(self) -> int:
+        return self.outs.data_ptr() + 8
+
+    @property
+    def flag_ptr(self) -> int:
+        return self.outs.data_ptr() + 12
+
+    def _marshal(self):
+        """Pre-build the ctypes arguments of every call of the step."""
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        self._g = []
+        for bi, b in enumerate(self.gather_buckets):
+            ids = (I64 * len(b))(*b)
+            chunks = (P * self.N)(*[self.chunk_ptr(bi, v) for v in range(self.N)])
+            fo = self.bucket_meta[bi][0]
+            self._g.append((len(b), ids, self.chunk_ptr(bi, self.rank), chunks,
+                            self.full.data_ptr() + 2 * fo))
+        self._r = []
+        for b in self.reduce_buckets:
+            ids = (I64 * len(b))(*b)
+            src = (P * (len(b) * self.N))(*[self.recv_ptr(v, d) for d in b for v in range(self.N)])
+            self._r.append((len(b), ids, src))
+        all_ids = [p["ds_id"] for p in self.params]
+        self._p = (len(all_ids), (I64 * len(all_ids))(*all_ids),
+                   (P * len(all_ids))(*[self.full_param_ptr(d) for d in all_ids]))
+
+    # ------------------------------------------------------------- phases
+    def _stream(self) -> int:
+        return int(self.torch.cuda.current_stream().cuda_stream)
+
+    def _ok(self, st):
+        if st != 0:
+            raise zs.Zs3Error(st, zs.zs3_last_error())
+
+    def pack(self, bi: int, stream=None):
+        n, ids, own, chunks, fullp = self._g[bi]
+        self._ok(zs.lib().zs3_gather_coalesced(self.h, self.rank, self.dcode, zs.ZS3_PACK, n, ids,
+                                               self.shard.data_ptr(), own, None, None, None,
+                                               stream if stream is not None else self._stream()))
+
+    def unpack(self, bi: int, stream=None):
+        n, ids, own, chunks, fullp = self._g[bi]
+        self._ok(zs.lib().zs3_gather_coalesced(self.h, self.rank, self.dcode, zs.ZS3_UNPACK, n, ids, None, None,
+                                               chunks, fullp, None,
+                                               stream if stream is not None else self._stream()))
+
+    def gather_pass(self, stream=None, on_unpack=None):
+        s = stream if stream is not None else self._stream()
+        for bi in range(len(self._g)):
+            self.pack(bi, s)
+            if on_unpack is not None:
+                on_unpack(True)
+            self.unpack(bi, s)
+            if on_unpack is not None:
+                on_unpack(False)
+
+    def reduce_scatter(self, stream=None):
+        s = stream if stream is not None else self._stream()
+        lib = zs.lib()
+        for n, ids, src in self._r:
+            self._ok(lib.zs3_reduce_scatter_local(self.h, self.rank, self.dcode, n, ids, src,
+                                                  self.grad.data_ptr(), s))
+
+    def repartition(self, stream=None):
+        n, ids, ptrs = self._p
+        self._ok(zs.lib().zs3_partition(self.h, self.rank, self.dcode, n, ids, ptrs, self.shard.data_ptr(),
+                                        stream if stream is not None else self._stream()))
+
+    def grad_norm(self, finalize: bool = True, stream=None):
+        self._ok(zs.lib().zs3_grad_norm(self.h, self.rank, self.dcode, self.grad.data_ptr(), self.sumsq.data_ptr(),
+                                        int(finalize), self.max_norm, 1.0, self.norm_ptr, self.scale_ptr,
+                                        self.flag_ptr, stream if stream is not None else self._stream()))
+
+    def adam_step(self, t: int, stream=None):
+        a = self.adam
+        hp = zs.zs3_adam_params(a.lr, a.beta1, a.beta2, a.eps, a.weight_decay, int(t))
+        s = stream if stream is not None else self._stream()
+        for b, e in self.sub_groups:
+            self._ok(zs.lib().zs3_adam_step(self.h, self.rank, self.dcode, b, e, self.master.data_ptr(),
+                                            self.exp_avg.data_ptr(), self.exp_avg_sq.data_ptr(),
+                                            self.grad.data_ptr(), self.shard.data_ptr(), self.scale_ptr,
+                                            self.flag_ptr, ctypes.byref(hp), s))
+
+    def step(self, stream=None, on_phase=None, on_unpack=None):
+        """One whole shard step; ``on_phase(name)`` is called before each phase
+        and with None at the end (for event timing)."""
+        self.t += 1
+        mark = on_phase or (lambda name: None)
+        mark("gather_fwd")
+        self.gather_pass(stream, on_unpack)
+        mark("gather_bwd")
+        self.gather_pass(stream, on_unpack)
+        mark("reduce_scatter")
+        self.reduce_scatter(stream)
+        mark("partition")
+        self.repartition(stream)
+        mark("grad_norm")
+        self.grad_norm(True, stream)
+        mark("adam")
+        self.adam_step(self.t, stream)
+        mark(None)
+
+    # ------------------------------------------------------------ set-up
+    def init_from_full(self):
+        """Partition the gathered/persistent full parameters into the shard,
+        fill every virtual rank's chunk of every wire buffer (what the
+        all-gather would deliver), and widen the shard into the fp32 master."""
+        torch = self.torch
+        tmp = torch.zeros_like(self.shard)
+        n, ids, ptrs = self._p
+        lib = zs.lib()
+        s = self._stream()
+        for v in range(self.N):
+            target = self.shard if v == self.rank else tmp
+            self._ok(lib.zs3_partition(self.h, v, self.dcode, n, ids, ptrs, target.data_ptr(), s))
+            for bi, (bn, bids, _, _, _) in enumerate(self._g):
+                self._ok(lib.zs3_gather_coalesced(self.h, v, self.dcode, zs.ZS3_PACK, bn, bids, target.data_ptr(),
+                                                  self.chunk_ptr(bi, v), None, None, None, s))
+        tdt = torch.float16 if self.dtype == "fp16" else torch.bfloat16
+        self.master.copy_(self.shard.view(tdt).to(torch.float32))
+        self.exp_avg.zero_()
+        self.exp_avg_sq.zero_()
+        del tmp
+
+    def fill_peer_norms(self):
+        """Stand-in for the N-scalar all-reduce of the norm: after one partial
+        on this rank, give every other rank the same partial sum."""
+        self.grad_norm(finalize=False)
+        self.sumsq[: self.N] = self.sumsq[self.rank].item()
+
+    # --------------------------------------------------------- accounting
+    def algorithmic_bytes(self) -> Dict[str, int]:
+        """Bytes each part of the step must move (real elements only)."""
+        N = self.N
+        part_real = sum(p["own"][1] - p["own"][0] for p in self.params if not p["persistent"])
+        own = self.own_real
+        F = self.F
+        return {
+            "pack": 2 * 4 * part_real,          # two passes, read + write of the real own shard elements
+            "unpack": 2 * 4 * F,                # two passes, read N pieces + write the full parameters
+            "reduce_scatter": 2 * N * own + 2 * own,
+            "partition": 4 * own,
+            "grad_norm": 2 * own,
+            "adam": 28 * own,
+        }
+
+    def destroy(self):
+        if self.h:
+            zs.zs3_layout_destroy(self.h)
+            self.h = None
