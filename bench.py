@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=12, help="decoder layers in the oracle's sample")
-    ap.add_argument("--no-kernel-events", action="store_true")
+    ap.add_argument("--rs-streams", type=int, default=4, help="streams the gradient buckets are spread over")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -61,9 +61,9 @@ def source_digest() -> str:
 
 
 def traffic_entry(config: str):
-    """HBM bytes per unpack launch from the committed counter summary, if it
+    """HBM bytes per gather launch from the committed counter summary, if it
     was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"unpack_traffic_{config}.json")
+    path = os.path.join(ROOT, "profiles", f"gather_traffic_{config}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -73,14 +73,14 @@ def traffic_entry(config: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def make_step(cfg, rank):
+def make_step(cfg, rank, rs_streams=4):
     from zero_sharded_state_amd.shard_step import AdamConfig, ShardStep
 
     return ShardStep(world_size=cfg.world_size, rank=rank, threshold=cfg.threshold, ds_ids=cfg.ds_ids,
                      numels=cfg.numels, dtype=cfg.dtype, prefetch_bucket_size=cfg.prefetch_bucket_size,
                      reduce_bucket_size=cfg.reduce_bucket_size, sub_group_size=cfg.sub_group_size,
                      adam=AdamConfig(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay),
-                     max_norm=cfg.max_norm)
+                     max_norm=cfg.max_norm, rs_streams=rs_streams)
 
 
 def fill_inputs(step, cfg):
@@ -206,7 +206,7 @@ def main():
     cfg = get_config(args.config)
     rank = cfg.bench_rank if args.rank is None else args.rank
     log(f"config {cfg.name}: {cfg.title}, rank {rank}")
-    step = make_step(cfg, rank)
+    step = make_step(cfg, rank, args.rs_streams)
     log(f"layout: S+P={step.S:,} own real={step.own_real:,} F={step.F:,} gather buckets={len(step.gather_buckets)} "
         f"reduce buckets={len(step.reduce_buckets)} sub-groups={len(step.sub_groups)}")
     t0 = time.time()
@@ -221,7 +221,6 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     phase_events = []
-    unpack_events = []
     stream = torch.cuda.current_stream()
 
     def on_phase(name):
@@ -229,19 +228,11 @@ def main():
         e.record(stream)
         phase_events[-1].append((name, e))
 
-    def on_unpack(start):
-        e = ev()
-        e.record(stream)
-        if start:
-            unpack_events.append([e, None])
-        else:
-            unpack_events[-1][1] = e
-
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(args.steps):
         phase_events.append([])
-        step.step(on_phase=on_phase, on_unpack=None if args.no_kernel_events else on_unpack)
+        step.step(on_phase=on_phase)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     log(f"timed {args.steps} steps in {wall:.3f} s")
@@ -267,17 +258,21 @@ def main():
         kernels[name] = {"ms": round(ms, 4), "bytes": phase_bytes[name],
                          "GBps": round(phase_bytes[name] / (ms * 1e-3) / 1e9, 1)}
 
-    roofline = None
-    if unpack_events:
-        durs = [a.elapsed_time(b) for a, b in unpack_events]
-        per_launch_bytes = nbytes["unpack"] / (2 * len(step.gather_buckets))
-        avg_ms = sum(durs) / len(durs)
-        achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
-        traffic = traffic_entry(cfg.name)
-        roofline = {"kernel": "unpack (k_copy<3>)", "bound": "hbm", "achieved": round(achieved, 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": traffic, "launches": len(durs), "avg_launch_ms": round(avg_ms, 5),
-                    "algorithmic_bytes_per_launch": int(per_launch_bytes)}
+    # Roofline entry of the dominant kernel: the fused gather (pack + unpack
+    # of one bucket, k_copy<4>), launched back to back on one stream in the
+    # two gather phases; its average launch duration is the phases' event
+    # time over the launch count.
+    launches = 2 * len(step.gather_buckets) * args.steps
+    gather_ms = sum(phases.get(k, 0.0) for k in ("gather_fwd", "gather_bwd"))
+    gather_bytes = nbytes["pack"] + nbytes["unpack"]
+    per_launch_bytes = gather_bytes / (2 * len(step.gather_buckets))
+    avg_ms = gather_ms / launches
+    achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
+    roofline = {"kernel": "gather: pack + unpack of one bucket (k_copy<4>)", "bound": "hbm",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_entry(cfg.name),
+                "launches": launches, "avg_launch_ms": round(avg_ms, 5),
+                "algorithmic_bytes_per_launch": int(per_launch_bytes)}
 
     if args.calibrate_copy_gib > 0:
         n = int(args.calibrate_copy_gib * 2**30) // 2

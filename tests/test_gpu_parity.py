@@ -72,7 +72,10 @@ def test_partition_bit_exact(prob, shift):
 
 @pytest.mark.parametrize("prob", PROBLEMS)
 @pytest.mark.parametrize("shifts", [(0, 0, 0), (1, 5, 2), (7, 0, 3)])
-def test_gather_pack_unpack_bit_exact(prob, shifts):
+@pytest.mark.parametrize("fused", [True, False])
+def test_gather_pack_unpack_bit_exact(prob, shifts, fused):
+    """fused: the wire's own slot is the pack output (one launch); otherwise
+    the own slot is a separate, already-filled chunk (pack, then unpack)."""
     seed, N, T, n, mx = prob
     s_shard, s_chunk, s_full = shifts
     ids, numels, full = _problem(seed, N, T, n, mx)
@@ -86,13 +89,14 @@ def test_gather_pack_unpack_bit_exact(prob, shifts):
             ref_chunks = [oracle.pack(L, v, bucket, shards[v]) for v in range(N)]
             ref_full, ref_offs = oracle.unpack(L, bucket, ref_chunks)
             r = (seed * 7) % N
-            note(f"gather seed={seed} N={N} rank={r} bucket={len(bucket)} params shifts={shifts}")
+            note(f"gather seed={seed} N={N} rank={r} bucket={len(bucket)} params shifts={shifts} fused={fused}")
             sh = Buf16(L.shard_numel, shift=s_shard, fill=shards[r])
             chunks = [Buf16(chunk_n, shift=(s_chunk + v) % 8, fill=ref_chunks[v]) for v in range(N)]
             own = Buf16(chunk_n, shift=s_chunk)
             fl = Buf16(full_n, shift=s_full)
             rank_ptrs = [c.ptr() for c in chunks]
-            rank_ptrs[r] = own.ptr()
+            if fused:
+                rank_ptrs[r] = own.ptr()
             offs = zs.zs3_gather_coalesced(h, r, "bf16", zs.ZS3_PACK | zs.ZS3_UNPACK, req, sh.ptr(), own.ptr(),
                                            rank_ptrs, fl.ptr())
             sync()

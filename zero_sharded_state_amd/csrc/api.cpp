@@ -98,6 +98,7 @@ struct Plan {
     size_t bytes = 0;
     int64_t n_pieces = 0;
     int64_t n_part = 0;           // norm: spans [0, n_part) are partitioned
+    int64_t n_blocks = 0;         // norm: workgroups of the sum-of-squares pass
     bool co_aligned = true;       // reduce-scatter: every source co-aligned with its dst
     size_t off_segs = 0, off_pieces = 0, off_srcs = 0, off_scratch = 0;
 
@@ -105,7 +106,7 @@ struct Plan {
     T* at(size_t off) const { return reinterpret_cast<T*>(static_cast<char*>(dev) + off); }
 };
 
-enum Op : int64_t { kOpPartition = 1, kOpPack, kOpUnpack, kOpReduce, kOpNorm, kOpAdam };
+enum Op : int64_t { kOpPartition = 1, kOpPack, kOpUnpack, kOpReduce, kOpNorm, kOpAdam, kOpGather };
 
 constexpr size_t kMaxPlans = 1 << 14;
 
@@ -248,8 +249,9 @@ zs3_status store_plan(zs3_layout* L, Key&& key, Plan&& plan, Plan** out) {
     return ZS3_OK;
 }
 
-zs3_status check_grid(int64_t n_pieces) {
-    if (n_pieces * kBlock >= (int64_t(1) << 32)) return fail(ZS3_EINVAL, "request too large for one launch");
+// Workgroups of one launch: n_pieces * sub must fit a 32-bit grid of work-items.
+zs3_status check_grid(int64_t n_pieces, int sub) {
+    if (n_pieces * sub * kBlock >= (int64_t(1) << 32)) return fail(ZS3_EINVAL, "request too large for one launch");
     return ZS3_OK;
 }
 
@@ -280,7 +282,7 @@ zs3_status build_copy_plan(zs3_layout* L, Key&& key, const std::vector<CopySeg>&
     std::vector<Piece> pieces;
     for (size_t i = 0; i < segs.size(); ++i)
         add_pieces(&pieces, static_cast<int32_t>(i), reinterpret_cast<uintptr_t>(segs[i].dst), segs[i].count, kCopyPiece);
-    zs3_status s = check_grid(static_cast<int64_t>(pieces.size()));
+    zs3_status s = check_grid(static_cast<int64_t>(pieces.size()), kCopySub);
     if (s != ZS3_OK) return s;
     Plan plan;
     plan.n_pieces = static_cast<int64_t>(pieces.size());
@@ -576,6 +578,39 @@ zs3_status zs3_gather_coalesced(zs3_layout_t L, int32_t rank, int32_t dtype, int
         for (int32_t i = 0; i < n; ++i) full_offsets[i] = f[i];
     if (n == 0) return ok();
 
+    // Pack and unpack in one launch when the wire's own slot is the pack's
+    // output: the own rank's part of the unpack then equals the shard's
+    // partitions, so it is read from the shard and both run together.
+    if (do_pack && do_unpack && rank_chunks[rank] == own_chunk) {
+        Key key{{kOpGather, device_id(), rank, reinterpret_cast<int64_t>(shard_flat),
+                 reinterpret_cast<int64_t>(own_chunk), reinterpret_cast<int64_t>(full_flat)}};
+        for (int32_t v = 0; v < N; ++v) key.w.push_back(reinterpret_cast<int64_t>(rank_chunks[v]));
+        for (int32_t k : order) key.w.push_back(L->params[pos[k]].ds_id);
+        Plan* plan = find_plan(L, key);
+        if (plan == nullptr) {
+            std::vector<CopySeg> segs;
+            const uint16_t* shard = static_cast<const uint16_t*>(shard_flat);
+            uint16_t* own = static_cast<uint16_t*>(own_chunk);
+            uint16_t* dst = static_cast<uint16_t*>(full_flat);
+            for (int32_t k : order) {
+                const Slot& p = L->params[pos[k]];
+                segs.push_back(CopySeg{shard + p.offset, own + c[k], p.ps, 0});
+            }
+            for (int32_t k : order) {
+                const Slot& p = L->params[pos[k]];
+                for (int32_t v = 0; v < N; ++v) {
+                    int64_t lo, hi;
+                    p.own_range(v, &lo, &hi);
+                    const uint16_t* src = v == rank ? shard + p.offset
+                                                    : static_cast<const uint16_t*>(rank_chunks[v]) + c[k];
+                    segs.push_back(CopySeg{src, dst + f[k] + lo, hi - lo, 0});
+                }
+            }
+            if ((s = build_copy_plan(L, std::move(key), segs, &plan)) != ZS3_OK) return s;
+        }
+        return run_copy(kCopyGather, plan, stream);
+    }
+
     if (do_pack) {
         Key key{{kOpPack, device_id(), rank, reinterpret_cast<int64_t>(shard_flat), reinterpret_cast<int64_t>(own_chunk)}};
         for (int32_t k : order) key.w.push_back(L->params[pos[k]].ds_id);
@@ -669,7 +704,7 @@ zs3_status zs3_reduce_scatter_local(zs3_layout_t L, int32_t rank, int32_t dtype,
             }
             add_pieces(&pieces, si, reinterpret_cast<uintptr_t>(dst), p.ps, kRsPiece);
         }
-        if ((s = check_grid(static_cast<int64_t>(pieces.size()))) != ZS3_OK) return s;
+        if ((s = check_grid(static_cast<int64_t>(pieces.size()), kRsSub)) != ZS3_OK) return s;
         Plan np;
         np.n_pieces = static_cast<int64_t>(pieces.size());
         np.co_aligned = co;
@@ -727,18 +762,20 @@ zs3_status zs3_grad_norm(zs3_layout_t L, int32_t rank, int32_t dtype, const void
         for (auto& r : part) add_spans(&spans, r.first, r.second, ((16u - ((base + 2 * r.first) & 15u)) & 15u) >> 1, kNormPiece);
         const int64_t n_part = static_cast<int64_t>(spans.size());
         for (auto& r : pers) add_spans(&spans, r.first, r.second, ((16u - ((base + 2 * r.first) & 15u)) & 15u) >> 1, kNormPiece);
-        if ((s = check_grid(static_cast<int64_t>(spans.size()))) != ZS3_OK) return s;
         Plan np;
         np.n_pieces = static_cast<int64_t>(spans.size());
         np.n_part = n_part;
+        np.n_blocks = std::min<int64_t>(np.n_pieces * kNormSub, kNormGrid);
         std::vector<size_t> offs;
-        s = upload(&np, {{spans.data(), spans.size() * sizeof(Span)}}, std::max<size_t>(8, spans.size() * sizeof(double)), &offs);
+        s = upload(&np, {{spans.data(), spans.size() * sizeof(Span)}},
+                   std::max<size_t>(16, 2 * static_cast<size_t>(np.n_blocks) * sizeof(double)), &offs);
         if (s != ZS3_OK) return s;
         np.off_pieces = offs[0];
         store_plan(L, std::move(key), std::move(np), &plan);
     }
     return hip_status(launch_grad_norm(dtype, static_cast<const uint16_t*>(grad_flat), plan->at<Span>(plan->off_pieces),
-                                       plan->n_pieces, plan->n_part, plan->at<double>(plan->off_scratch), sumsq, rank,
+                                       plan->n_pieces, plan->n_part, plan->n_blocks, plan->at<double>(plan->off_scratch),
+                                       sumsq, rank,
                                        L->world, finalize, max_norm, loss_scale, norm_out, scale_out, nonfinite,
                                        static_cast<hipStream_t>(stream)),
                       "grad-norm kernel launch");
@@ -802,7 +839,7 @@ zs3_status zs3_adam_step(zs3_layout_t L, int32_t rank, int32_t dtype, int64_t be
         }
         std::vector<Span> spans;
         for (auto& r : runs) add_spans(&spans, r.first, r.second, (8 - (r.first & 7)) & 7, kAdamPiece);
-        if ((s = check_grid(static_cast<int64_t>(spans.size()))) != ZS3_OK) return s;
+        if ((s = check_grid(static_cast<int64_t>(spans.size()), kAdamSub)) != ZS3_OK) return s;
         Plan np;
         np.n_pieces = static_cast<int64_t>(spans.size());
         std::vector<size_t> offs;

@@ -25,6 +25,9 @@ namespace {
 
 // ---------------------------------------------------------------- 16-bit
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 template <int D>
 __device__ __forceinline__ float widen(uint32_t bits16);
 
@@ -59,8 +62,31 @@ __device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xffffu; }
 __device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
 __device__ __forceinline__ uint32_t pack2(uint32_t a, uint32_t b) { return a | (b << 16); }
 
-__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
-    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+// Streaming 16-byte loads and stores, non-temporal when NT: every byte of
+// these kernels is touched once per call.
+template <bool NT>
+__device__ __forceinline__ v4u ld_stream(const void* p) {
+    const v4u* q = reinterpret_cast<const v4u*>(p);
+    if constexpr (NT) return __builtin_nontemporal_load(q);
+    else return *q;
+}
+template <bool NT>
+__device__ __forceinline__ void st_stream(void* p, v4u v) {
+    v4u* q = reinterpret_cast<v4u*>(p);
+    if constexpr (NT) __builtin_nontemporal_store(v, q);
+    else *q = v;
+}
+template <bool NT>
+__device__ __forceinline__ v4f ld_stream_f(const float* p) {
+    const v4f* q = reinterpret_cast<const v4f*>(p);
+    if constexpr (NT) return __builtin_nontemporal_load(q);
+    else return *q;
+}
+template <bool NT>
+__device__ __forceinline__ void st_stream_f(float* p, v4f v) {
+    v4f* q = reinterpret_cast<v4f*>(p);
+    if constexpr (NT) __builtin_nontemporal_store(v, q);
+    else *q = v;
 }
 
 // Elements before `p` reaches 16-byte alignment (p is 2-byte aligned).
@@ -71,18 +97,19 @@ __device__ __forceinline__ int64_t head16(const void* p) {
 // 16 bytes of 16-bit data starting at p, whose byte address is SO (mod 16).
 // SO != 0 reads the two aligned 16-byte blocks that hold those bytes and
 // shifts; both blocks contain bytes of the requested range, so neither can
-// cross into a page the range does not touch.
-template <int SO>
-__device__ __forceinline__ uint4 load_shift(const uint16_t* p) {
+// cross into a page the range does not touch.  (Plain loads: the second
+// block is the next lane's first and should hit in cache.)
+template <int SO, bool NT>
+__device__ __forceinline__ v4u load_shift(const uint16_t* p) {
     if constexpr (SO == 0) {
-        return *reinterpret_cast<const uint4*>(p);
+        return ld_stream<NT>(p);
     } else {
-        const uint4* a = reinterpret_cast<const uint4*>(reinterpret_cast<uintptr_t>(p) - SO);
-        const uint4 lo = a[0];
-        const uint4 hi = a[1];
+        const v4u* a = reinterpret_cast<const v4u*>(reinterpret_cast<uintptr_t>(p) - SO);
+        const v4u lo = a[0];
+        const v4u hi = a[1];
         const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         constexpr int d = SO / 4;
-        uint4 r;
+        v4u r;
         if constexpr (SO % 4 == 0) {
             r.x = w[d]; r.y = w[d + 1]; r.z = w[d + 2]; r.w = w[d + 3];
         } else {
@@ -97,16 +124,17 @@ __device__ __forceinline__ uint4 load_shift(const uint16_t* p) {
 
 // Runtime-offset variant: `so` is uniform across the workgroup, so the
 // switch is a scalar branch.
-__device__ __forceinline__ uint4 load_any(const uint16_t* p, uint32_t so) {
+template <bool NT>
+__device__ __forceinline__ v4u load_any(const uint16_t* p, uint32_t so) {
     switch (so) {
-        case 0: return load_shift<0>(p);
-        case 2: return load_shift<2>(p);
-        case 4: return load_shift<4>(p);
-        case 6: return load_shift<6>(p);
-        case 8: return load_shift<8>(p);
-        case 10: return load_shift<10>(p);
-        case 12: return load_shift<12>(p);
-        default: return load_shift<14>(p);
+        case 0: return load_shift<0, NT>(p);
+        case 2: return load_shift<2, NT>(p);
+        case 4: return load_shift<4, NT>(p);
+        case 6: return load_shift<6, NT>(p);
+        case 8: return load_shift<8, NT>(p);
+        case 10: return load_shift<10, NT>(p);
+        case 12: return load_shift<12, NT>(p);
+        default: return load_shift<14, NT>(p);
     }
 }
 
@@ -114,29 +142,34 @@ __device__ __forceinline__ uint4 load_any(const uint16_t* p, uint32_t so) {
 // Partition ([codex] 3.1: own range into the shard, padding zeroed), pack
 // and unpack ([codex] 5.2: ds_id-ordered flat chunk, then per-parameter
 // views of the gathered buffer) are all lists of contiguous copies; the
-// host turns each call into segments and pieces.
+// host turns each call into segments and pieces.  kCopySub workgroups share
+// a piece: after the piece's head elements (until the destination is
+// 16-byte aligned, done by sub-block 0), sub-block `sub` moves vectors
+// [sub*B*V, (sub+1)*B*V) and the last one the tail elements.
 
 template <int SO>
-__device__ __forceinline__ void copy_body(const uint16_t* src, uint4* dst, int64_t nv, int t) {
-    uint4 r[kCopyVPT];
+__device__ __forceinline__ void copy_body(const uint16_t* src, uint16_t* dst, int64_t i0, int64_t nv, int t) {
+    v4u r[kCopyVPT];
 #pragma unroll
     for (int u = 0; u < kCopyVPT; ++u) {
-        const int64_t i = t + int64_t(u) * kBlock;
-        if (i < nv) r[u] = load_shift<SO>(src + 8 * i);
+        const int64_t i = i0 + t + int64_t(u) * kBlock;
+        if (i < nv) r[u] = load_shift<SO, kNtCopy>(src + 8 * i);
     }
 #pragma unroll
     for (int u = 0; u < kCopyVPT; ++u) {
-        const int64_t i = t + int64_t(u) * kBlock;
-        if (i < nv) dst[i] = r[u];
+        const int64_t i = i0 + t + int64_t(u) * kBlock;
+        if (i < nv) st_stream<kNtCopy>(dst + 8 * i, r[u]);
     }
 }
 
-// One body, three kernel names (partition, pack, unpack) so that profiles
-// attribute time to each step of the method.
+// One body, four kernel names (partition, pack, unpack, fused gather) so
+// that profiles attribute time to each step of the method.
 template <int OP>
 __global__ __launch_bounds__(kBlock) void k_copy(const CopySeg* __restrict__ segs,
                                                  const Piece* __restrict__ pieces) {
-    const Piece pc = pieces[blockIdx.x];
+    const uint32_t pidx = blockIdx.x / kCopySub;
+    const int sub = static_cast<int>(blockIdx.x % kCopySub);
+    const Piece pc = pieces[pidx];
     const CopySeg sg = segs[pc.seg];
     const int t = threadIdx.x;
     uint16_t* dst = sg.dst + pc.begin;
@@ -144,40 +177,40 @@ __global__ __launch_bounds__(kBlock) void k_copy(const CopySeg* __restrict__ seg
     int64_t n = pc.len;
     int64_t h = head16(dst);
     if (h > n) h = n;
-    if (t < h) dst[t] = src != nullptr ? src[t] : uint16_t(0);
+    if (sub == 0 && t < h) dst[t] = src != nullptr ? src[t] : uint16_t(0);
     dst += h;
     n -= h;
     if (src != nullptr) src += h;
     const int64_t nv = n >> 3;
-    uint4* dv = reinterpret_cast<uint4*>(dst);
+    const int64_t i0 = int64_t(sub) * kBlock * kCopyVPT;
     if (src == nullptr) {
-        const uint4 z = make_uint4(0, 0, 0, 0);
+        const v4u z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int u = 0; u < kCopyVPT; ++u) {
-            const int64_t i = t + int64_t(u) * kBlock;
-            if (i < nv) dv[i] = z;
+            const int64_t i = i0 + t + int64_t(u) * kBlock;
+            if (i < nv) st_stream<kNtCopy>(dst + 8 * i, z);
         }
     } else {
         switch (static_cast<uint32_t>(reinterpret_cast<uintptr_t>(src)) & 15u) {
-            case 0: copy_body<0>(src, dv, nv, t); break;
-            case 2: copy_body<2>(src, dv, nv, t); break;
-            case 4: copy_body<4>(src, dv, nv, t); break;
-            case 6: copy_body<6>(src, dv, nv, t); break;
-            case 8: copy_body<8>(src, dv, nv, t); break;
-            case 10: copy_body<10>(src, dv, nv, t); break;
-            case 12: copy_body<12>(src, dv, nv, t); break;
-            default: copy_body<14>(src, dv, nv, t); break;
+            case 0: copy_body<0>(src, dst, i0, nv, t); break;
+            case 2: copy_body<2>(src, dst, i0, nv, t); break;
+            case 4: copy_body<4>(src, dst, i0, nv, t); break;
+            case 6: copy_body<6>(src, dst, i0, nv, t); break;
+            case 8: copy_body<8>(src, dst, i0, nv, t); break;
+            case 10: copy_body<10>(src, dst, i0, nv, t); break;
+            case 12: copy_body<12>(src, dst, i0, nv, t); break;
+            default: copy_body<14>(src, dst, i0, nv, t); break;
         }
     }
     const int64_t rem = n & 7;
-    if (t < rem) dst[nv * 8 + t] = src != nullptr ? src[nv * 8 + t] : uint16_t(0);
+    if (sub == kCopySub - 1 && t < rem) dst[nv * 8 + t] = src != nullptr ? src[nv * 8 + t] : uint16_t(0);
 }
 
 // ---------------------------------------------------- reduce-scatter kernel
 // [codex] 6.2 / [csdn] step 3: own slice of the average of the N ranks'
 // gradients.  Each output element is ((0 + g_0) + g_1 + ... + g_{N-1}) / N
 // in fp32, ranks in order, then rounded to the 16-bit type; padding
-// positions get 0.
+// positions get 0.  Pieces are split among kRsSub workgroups as in k_copy.
 
 struct Divider {
     float n;        // N as float
@@ -203,7 +236,9 @@ __global__ __launch_bounds__(kBlock) void k_reduce_scatter(const RsSeg* __restri
                                                            const Piece* __restrict__ pieces,
                                                            const uint16_t* const* __restrict__ srcs,
                                                            int world, Divider div) {
-    const Piece pc = pieces[blockIdx.x];
+    const uint32_t pidx = blockIdx.x / kRsSub;
+    const int sub = static_cast<int>(blockIdx.x % kRsSub);
+    const Piece pc = pieces[pidx];
     const RsSeg sg = segs[pc.seg];
     const int t = threadIdx.x;
     const uint16_t* const* sp = srcs + sg.src_index;
@@ -212,72 +247,74 @@ __global__ __launch_bounds__(kBlock) void k_reduce_scatter(const RsSeg* __restri
     uint16_t* dst = sg.dst + k0;
     int64_t h = head16(dst);
     if (h > n) h = n;
-    if (t < h) dst[t] = rs_elem<D>(sp, world, div, k0 + t, sg.real);
+    if (sub == 0 && t < h) dst[t] = rs_elem<D>(sp, world, div, k0 + t, sg.real);
     k0 += h;
     dst += h;
     n -= h;
     const int64_t nv = n >> 3;
     int64_t nfull = sg.real > k0 ? (sg.real - k0) >> 3 : 0;
     if (nfull > nv) nfull = nv;
+    const int64_t i0 = int64_t(sub) * kBlock * kRsVPT;
 
-    float acc[kRsVPT][8];
+    if (i0 + t < nfull) {
+        float acc[kRsVPT][8];
 #pragma unroll
-    for (int u = 0; u < kRsVPT; ++u)
+        for (int u = 0; u < kRsVPT; ++u)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
-
-    if (t < nfull) {
+            for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
 #pragma unroll 4
         for (int v = 0; v < world; ++v) {
             const uint16_t* s = sp[v] + k0;
-            uint4 x[kRsVPT];
+            v4u x[kRsVPT];
             if constexpr (ALIGNED) {
 #pragma unroll
                 for (int u = 0; u < kRsVPT; ++u) {
-                    const int64_t i = t + int64_t(u) * kBlock;
-                    if (i < nfull) x[u] = reinterpret_cast<const uint4*>(s)[i];
+                    const int64_t i = i0 + t + int64_t(u) * kBlock;
+                    if (i < nfull) x[u] = ld_stream<kNtRs>(s + 8 * i);
                 }
             } else {
                 const uint32_t so = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s)) & 15u;
 #pragma unroll
                 for (int u = 0; u < kRsVPT; ++u) {
-                    const int64_t i = t + int64_t(u) * kBlock;
-                    if (i < nfull) x[u] = load_any(s + 8 * i, so);
+                    const int64_t i = i0 + t + int64_t(u) * kBlock;
+                    if (i < nfull) x[u] = load_any<kNtRs>(s + 8 * i, so);
                 }
             }
 #pragma unroll
             for (int u = 0; u < kRsVPT; ++u) {
-                const int64_t i = t + int64_t(u) * kBlock;
+                const int64_t i = i0 + t + int64_t(u) * kBlock;
                 if (i < nfull) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const uint32_t w = word(x[u], q);
+                        const uint32_t w = x[u][q];
                         acc[u][2 * q] += widen<D>(lo16(w));
                         acc[u][2 * q + 1] += widen<D>(hi16(w));
                     }
                 }
             }
         }
-        uint4* dv = reinterpret_cast<uint4*>(dst);
 #pragma unroll
         for (int u = 0; u < kRsVPT; ++u) {
-            const int64_t i = t + int64_t(u) * kBlock;
+            const int64_t i = i0 + t + int64_t(u) * kBlock;
             if (i < nfull) {
-                uint4 o;
+                v4u o;
                 o.x = pack2(narrow<D>(div(acc[u][0])), narrow<D>(div(acc[u][1])));
                 o.y = pack2(narrow<D>(div(acc[u][2])), narrow<D>(div(acc[u][3])));
                 o.z = pack2(narrow<D>(div(acc[u][4])), narrow<D>(div(acc[u][5])));
                 o.w = pack2(narrow<D>(div(acc[u][6])), narrow<D>(div(acc[u][7])));
-                dv[i] = o;
+                st_stream<kNtRs>(dst + 8 * i, o);
             }
         }
     }
-    // vectors that hold padding (the partial one and those past it)
-    for (int64_t i = nfull + t; i < nv; i += kBlock) {
+    // this sub-block's vectors that hold padding (the partial one and those past it)
+    int64_t lo = i0 > nfull ? i0 : nfull;
+    int64_t hi = i0 + int64_t(kBlock) * kRsVPT;
+    if (hi > nv) hi = nv;
+    for (int64_t i = lo + t; i < hi; i += kBlock) {
         for (int e = 0; e < 8; ++e) dst[8 * i + e] = rs_elem<D>(sp, world, div, k0 + 8 * i + e, sg.real);
     }
     const int64_t rem = n & 7;
-    if (t < rem) dst[nv * 8 + t] = rs_elem<D>(sp, world, div, k0 + nv * 8 + t, sg.real);
+    if (sub == kRsSub - 1 && t < rem) dst[nv * 8 + t] = rs_elem<D>(sp, world, div, k0 + nv * 8 + t, sg.real);
 }
 
 // ------------------------------------------------------------ grad norm
@@ -313,58 +350,72 @@ __device__ __forceinline__ double sq(uint32_t bits16) {
     return x * x;
 }
 
+// Grid-stride over (span, sub-block) work items; each workgroup keeps one
+// sum for partitioned spans [0, n_part) and one for persistent spans and
+// writes them to partials[2*block], partials[2*block+1].
 template <int D>
 __global__ __launch_bounds__(kBlock) void k_sumsq(const uint16_t* __restrict__ grad,
-                                                  const Span* __restrict__ spans,
-                                                  double* __restrict__ partials) {
+                                                  const Span* __restrict__ spans, int64_t n_spans,
+                                                  int64_t n_part, double* __restrict__ partials) {
     __shared__ double sh[kBlock / 64];
-    const Span sp = spans[blockIdx.x];
     const int t = threadIdx.x;
-    const uint16_t* p = grad + sp.begin;
-    int64_t n = sp.len;
-    int64_t h = head16(p);
-    if (h > n) h = n;
-    double acc = 0.0;
-    if (t < h) acc += sq<D>(p[t]);
-    p += h;
-    n -= h;
-    const int64_t nv = n >> 3;
-    const uint4* pv = reinterpret_cast<const uint4*>(p);
-    uint4 x[kNormVPT];
+    double acc_part = 0.0, acc_pers = 0.0;
+    const int64_t W = n_spans * kNormSub;
+    for (int64_t w = blockIdx.x; w < W; w += gridDim.x) {
+        const int64_t si = w / kNormSub;
+        const int sub = static_cast<int>(w % kNormSub);
+        const Span sp = spans[si];
+        const uint16_t* p = grad + sp.begin;
+        int64_t n = sp.len;
+        int64_t h = head16(p);
+        if (h > n) h = n;
+        double acc = 0.0;
+        if (sub == 0 && t < h) acc += sq<D>(p[t]);
+        p += h;
+        n -= h;
+        const int64_t nv = n >> 3;
+        const int64_t i0 = int64_t(sub) * kBlock * kNormVPT;
+        v4u x[kNormVPT];
 #pragma unroll
-    for (int u = 0; u < kNormVPT; ++u) {
-        const int64_t i = t + int64_t(u) * kBlock;
-        if (i < nv) x[u] = pv[i];
-    }
+        for (int u = 0; u < kNormVPT; ++u) {
+            const int64_t i = i0 + t + int64_t(u) * kBlock;
+            if (i < nv) x[u] = ld_stream<kNtNorm>(p + 8 * i);
+        }
 #pragma unroll
-    for (int u = 0; u < kNormVPT; ++u) {
-        const int64_t i = t + int64_t(u) * kBlock;
-        if (i < nv) {
+        for (int u = 0; u < kNormVPT; ++u) {
+            const int64_t i = i0 + t + int64_t(u) * kBlock;
+            if (i < nv) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t w = word(x[u], q);
-                acc += sq<D>(lo16(w));
-                acc += sq<D>(hi16(w));
+                for (int q = 0; q < 4; ++q) {
+                    acc += sq<D>(lo16(x[u][q]));
+                    acc += sq<D>(hi16(x[u][q]));
+                }
             }
         }
+        const int64_t rem = n & 7;
+        if (sub == kNormSub - 1 && t < rem) acc += sq<D>(p[nv * 8 + t]);
+        if (si < n_part) acc_part += acc;
+        else acc_pers += acc;
     }
-    const int64_t rem = n & 7;
-    if (t < rem) acc += sq<D>(p[nv * 8 + t]);
-    const double s = block_sum(acc, sh);
-    if (t == 0) partials[blockIdx.x] = s;
+    const double a = block_sum(acc_part, sh);
+    const double b = block_sum(acc_pers, sh);
+    if (t == 0) {
+        partials[2 * blockIdx.x] = a;
+        partials[2 * blockIdx.x + 1] = b;
+    }
 }
 
-__global__ __launch_bounds__(kBlock) void k_norm_finalize(const double* __restrict__ partials,
-                                                          int64_t n_spans, int64_t n_part,
-                                                          double* __restrict__ sumsq, int rank,
-                                                          int world, int finalize, double max_norm,
-                                                          double loss_scale, double* norm_out,
-                                                          float* scale_out, int32_t* nonfinite) {
+__global__ __launch_bounds__(kBlock) void k_norm_finalize(const double* __restrict__ partials, int64_t n_blocks,
+                                                          double* __restrict__ sumsq, int rank, int world,
+                                                          int finalize, double max_norm, double loss_scale,
+                                                          double* norm_out, float* scale_out, int32_t* nonfinite) {
     __shared__ double sh[kBlock / 64];
     const int t = threadIdx.x;
     double a = 0.0, b = 0.0;
-    for (int64_t i = t; i < n_part; i += kBlock) a += partials[i];
-    for (int64_t i = n_part + t; i < n_spans; i += kBlock) b += partials[i];
+    for (int64_t i = t; i < n_blocks; i += kBlock) {
+        a += partials[2 * i];
+        b += partials[2 * i + 1];
+    }
     a = block_sum(a, sh);
     b = block_sum(b, sh);
     if (t == 0) {
@@ -427,67 +478,72 @@ __global__ __launch_bounds__(kBlock) void k_adam(const Span* __restrict__ spans,
                                                  const int32_t* __restrict__ nonfinite_p, AdamConsts c) {
     if (nonfinite_p != nullptr && *nonfinite_p != 0) return;
     const float scale = *scale_p;
-    const Span sp = spans[blockIdx.x];
+    const uint32_t pidx = blockIdx.x / kAdamSub;
+    const int sub = static_cast<int>(blockIdx.x % kAdamSub);
+    const Span sp = spans[pidx];
     const int t = threadIdx.x;
     int64_t b = sp.begin;
     int64_t n = sp.len;
     if constexpr (!VEC) {
-        for (int64_t i = t; i < n; i += kBlock) adam_scalar<D>(b + i, w, m, v, g, s, scale, c);
+        for (int64_t i = int64_t(sub) * kBlock + t; i < n; i += int64_t(kBlock) * kAdamSub)
+            adam_scalar<D>(b + i, w, m, v, g, s, scale, c);
         return;
     } else {
         int64_t h = (8 - (b & 7)) & 7;     // with 16-byte aligned bases, index % 8 == 0 is aligned for all
         if (h > n) h = n;
-        if (t < h) adam_scalar<D>(b + t, w, m, v, g, s, scale, c);
+        if (sub == 0 && t < h) adam_scalar<D>(b + t, w, m, v, g, s, scale, c);
         b += h;
         n -= h;
         const int64_t ng = n >> 3;
-        float4 W[kAdamGPT][2], M[kAdamGPT][2], V[kAdamGPT][2];
-        uint4 G[kAdamGPT];
+        const int64_t i0 = int64_t(sub) * kBlock * kAdamGPT;
+        v4f W[kAdamGPT][2], M[kAdamGPT][2], V[kAdamGPT][2];
+        v4u G[kAdamGPT];
 #pragma unroll
         for (int u = 0; u < kAdamGPT; ++u) {
-            const int64_t i = t + int64_t(u) * kBlock;
+            const int64_t i = i0 + t + int64_t(u) * kBlock;
             if (i < ng) {
                 const int64_t e = b + 8 * i;
-                W[u][0] = reinterpret_cast<const float4*>(w + e)[0];
-                W[u][1] = reinterpret_cast<const float4*>(w + e)[1];
-                M[u][0] = reinterpret_cast<const float4*>(m + e)[0];
-                M[u][1] = reinterpret_cast<const float4*>(m + e)[1];
-                V[u][0] = reinterpret_cast<const float4*>(v + e)[0];
-                V[u][1] = reinterpret_cast<const float4*>(v + e)[1];
-                G[u] = *reinterpret_cast<const uint4*>(g + e);
+                W[u][0] = ld_stream_f<kNtAdam>(w + e);
+                W[u][1] = ld_stream_f<kNtAdam>(w + e + 4);
+                M[u][0] = ld_stream_f<kNtAdam>(m + e);
+                M[u][1] = ld_stream_f<kNtAdam>(m + e + 4);
+                V[u][0] = ld_stream_f<kNtAdam>(v + e);
+                V[u][1] = ld_stream_f<kNtAdam>(v + e + 4);
+                G[u] = ld_stream<kNtAdam>(g + e);
             }
         }
 #pragma unroll
         for (int u = 0; u < kAdamGPT; ++u) {
-            const int64_t i = t + int64_t(u) * kBlock;
+            const int64_t i = i0 + t + int64_t(u) * kBlock;
             if (i < ng) {
                 const int64_t e = b + 8 * i;
-                float ww[8] = {W[u][0].x, W[u][0].y, W[u][0].z, W[u][0].w,
-                               W[u][1].x, W[u][1].y, W[u][1].z, W[u][1].w};
-                float mm[8] = {M[u][0].x, M[u][0].y, M[u][0].z, M[u][0].w,
-                               M[u][1].x, M[u][1].y, M[u][1].z, M[u][1].w};
-                float vv[8] = {V[u][0].x, V[u][0].y, V[u][0].z, V[u][0].w,
-                               V[u][1].x, V[u][1].y, V[u][1].z, V[u][1].w};
+                float ww[8], mm[8], vv[8];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    ww[q] = W[u][0][q]; ww[q + 4] = W[u][1][q];
+                    mm[q] = M[u][0][q]; mm[q + 4] = M[u][1][q];
+                    vv[q] = V[u][0][q]; vv[q + 4] = V[u][1][q];
+                }
                 uint32_t out[8];
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    const uint32_t gw = word(G[u], q >> 1);
+                    const uint32_t gw = G[u][q >> 1];
                     const float gf = widen<D>((q & 1) ? hi16(gw) : lo16(gw));
                     adam1(ww[q], mm[q], vv[q], gf, scale, c);
                     out[q] = narrow<D>(ww[q]);
                 }
-                reinterpret_cast<float4*>(w + e)[0] = make_float4(ww[0], ww[1], ww[2], ww[3]);
-                reinterpret_cast<float4*>(w + e)[1] = make_float4(ww[4], ww[5], ww[6], ww[7]);
-                reinterpret_cast<float4*>(m + e)[0] = make_float4(mm[0], mm[1], mm[2], mm[3]);
-                reinterpret_cast<float4*>(m + e)[1] = make_float4(mm[4], mm[5], mm[6], mm[7]);
-                reinterpret_cast<float4*>(v + e)[0] = make_float4(vv[0], vv[1], vv[2], vv[3]);
-                reinterpret_cast<float4*>(v + e)[1] = make_float4(vv[4], vv[5], vv[6], vv[7]);
-                *reinterpret_cast<uint4*>(s + e) = make_uint4(pack2(out[0], out[1]), pack2(out[2], out[3]),
-                                                              pack2(out[4], out[5]), pack2(out[6], out[7]));
+                st_stream_f<kNtAdam>(w + e, v4f{ww[0], ww[1], ww[2], ww[3]});
+                st_stream_f<kNtAdam>(w + e + 4, v4f{ww[4], ww[5], ww[6], ww[7]});
+                st_stream_f<kNtAdam>(m + e, v4f{mm[0], mm[1], mm[2], mm[3]});
+                st_stream_f<kNtAdam>(m + e + 4, v4f{mm[4], mm[5], mm[6], mm[7]});
+                st_stream_f<kNtAdam>(v + e, v4f{vv[0], vv[1], vv[2], vv[3]});
+                st_stream_f<kNtAdam>(v + e + 4, v4f{vv[4], vv[5], vv[6], vv[7]});
+                st_stream<kNtAdam>(s + e, v4u{pack2(out[0], out[1]), pack2(out[2], out[3]),
+                                     pack2(out[4], out[5]), pack2(out[6], out[7])});
             }
         }
         const int64_t rem = n & 7;
-        if (t < rem) adam_scalar<D>(b + ng * 8 + t, w, m, v, g, s, scale, c);
+        if (sub == kAdamSub - 1 && t < rem) adam_scalar<D>(b + ng * 8 + t, w, m, v, g, s, scale, c);
     }
 }
 
@@ -500,11 +556,12 @@ inline dim3 grid_of(int64_t n) { return dim3(static_cast<uint32_t>(n)); }
 hipError_t launch_copy(CopyKind kind, const CopySeg* segs, const Piece* pieces, int64_t n_pieces,
                        hipStream_t stream) {
     if (n_pieces <= 0) return hipSuccess;
-    const dim3 g = grid_of(n_pieces), b(kBlock);
+    const dim3 g = grid_of(n_pieces * kCopySub), b(kBlock);
     switch (kind) {
         case kCopyPartition: hipLaunchKernelGGL(k_copy<kCopyPartition>, g, b, 0, stream, segs, pieces); break;
         case kCopyPack: hipLaunchKernelGGL(k_copy<kCopyPack>, g, b, 0, stream, segs, pieces); break;
-        default: hipLaunchKernelGGL(k_copy<kCopyUnpack>, g, b, 0, stream, segs, pieces); break;
+        case kCopyUnpack: hipLaunchKernelGGL(k_copy<kCopyUnpack>, g, b, 0, stream, segs, pieces); break;
+        default: hipLaunchKernelGGL(k_copy<kCopyGather>, g, b, 0, stream, segs, pieces); break;
     }
     return hipGetLastError();
 }
@@ -517,7 +574,7 @@ hipError_t launch_reduce_scatter(int32_t dtype, const RsSeg* segs, const Piece* 
     div.n = static_cast<float>(world);
     div.pow2 = (world & (world - 1)) == 0;
     div.inv = 1.0f / static_cast<float>(world);
-    const dim3 g = grid_of(n_pieces), b(kBlock);
+    const dim3 g = grid_of(n_pieces * kRsSub), b(kBlock);
     if (dtype == kFP16) {
         if (co_aligned) hipLaunchKernelGGL((k_reduce_scatter<kFP16, true>), g, b, 0, stream, segs, pieces, srcs, world, div);
         else hipLaunchKernelGGL((k_reduce_scatter<kFP16, false>), g, b, 0, stream, segs, pieces, srcs, world, div);
@@ -529,17 +586,19 @@ hipError_t launch_reduce_scatter(int32_t dtype, const RsSeg* segs, const Piece* 
 }
 
 hipError_t launch_grad_norm(int32_t dtype, const uint16_t* grad, const Span* spans, int64_t n_spans,
-                            int64_t n_part, double* partials, double* sumsq, int32_t rank, int32_t world,
-                            int32_t finalize, double max_norm, double loss_scale, double* norm_out,
+                            int64_t n_part, int64_t n_blocks, double* partials, double* sumsq, int32_t rank,
+                            int32_t world, int32_t finalize, double max_norm, double loss_scale, double* norm_out,
                             float* scale_out, int32_t* nonfinite, hipStream_t stream) {
-    if (n_spans > 0) {
-        if (dtype == kFP16) hipLaunchKernelGGL(k_sumsq<kFP16>, grid_of(n_spans), dim3(kBlock), 0, stream, grad, spans, partials);
-        else hipLaunchKernelGGL(k_sumsq<kBF16>, grid_of(n_spans), dim3(kBlock), 0, stream, grad, spans, partials);
+    if (n_blocks > 0) {
+        if (dtype == kFP16)
+            hipLaunchKernelGGL(k_sumsq<kFP16>, grid_of(n_blocks), dim3(kBlock), 0, stream, grad, spans, n_spans, n_part, partials);
+        else
+            hipLaunchKernelGGL(k_sumsq<kBF16>, grid_of(n_blocks), dim3(kBlock), 0, stream, grad, spans, n_spans, n_part, partials);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_norm_finalize, dim3(1), dim3(kBlock), 0, stream, partials, n_spans, n_part, sumsq,
-                       rank, world, finalize, max_norm, loss_scale, norm_out, scale_out, nonfinite);
+    hipLaunchKernelGGL(k_norm_finalize, dim3(1), dim3(kBlock), 0, stream, partials, n_blocks, sumsq, rank, world,
+                       finalize, max_norm, loss_scale, norm_out, scale_out, nonfinite);
     return hipGetLastError();
 }
 
@@ -547,7 +606,7 @@ hipError_t launch_adam(int32_t dtype, const Span* spans, int64_t n_spans, float*
                        float* exp_avg_sq, const uint16_t* grad, uint16_t* shard, const float* scale,
                        const int32_t* nonfinite, const AdamConsts& c, bool vec_ok, hipStream_t stream) {
     if (n_spans <= 0) return hipSuccess;
-    const dim3 g = grid_of(n_spans), b(kBlock);
+    const dim3 g = grid_of(n_spans * kAdamSub), b(kBlock);
     if (dtype == kFP16) {
         if (vec_ok) hipLaunchKernelGGL((k_adam<kFP16, true>), g, b, 0, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
         else hipLaunchKernelGGL((k_adam<kFP16, false>), g, b, 0, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);

@@ -11,16 +11,67 @@ namespace zs3 {
 
 constexpr int kBlock = 256;             // threads per workgroup (4 wave64)
 
-// Elements of one workgroup's piece, per kernel family.  A piece is the
-// unit of the host-built work list: one workgroup handles exactly one.
-constexpr int kCopyVPT = 8;             // 16-byte vectors per thread
-constexpr int64_t kCopyPiece = int64_t(kBlock) * kCopyVPT * 8;
-constexpr int kRsVPT = 2;
-constexpr int64_t kRsPiece = int64_t(kBlock) * kRsVPT * 8;
-constexpr int kNormVPT = 8;
-constexpr int64_t kNormPiece = int64_t(kBlock) * kNormVPT * 8;
-constexpr int kAdamGPT = 2;             // groups of 8 elements per thread
-constexpr int64_t kAdamPiece = int64_t(kBlock) * kAdamGPT * 8;
+// Launch shape of each kernel family (tunable at build time).  A "piece" is
+// the unit of the host-built work list; SUB one-shot workgroups share a
+// piece, each moving VPT 16-byte vectors per thread.  Measured on MI355X,
+// short-lived workgroups with one or two vectors per thread and
+// non-temporal loads/stores stream HBM fastest.
+#ifndef ZS3_COPY_VPT
+#define ZS3_COPY_VPT 2
+#endif
+#ifndef ZS3_COPY_SUB
+#define ZS3_COPY_SUB 4
+#endif
+#ifndef ZS3_RS_VPT
+#define ZS3_RS_VPT 1
+#endif
+#ifndef ZS3_RS_SUB
+#define ZS3_RS_SUB 8
+#endif
+#ifndef ZS3_NORM_VPT
+#define ZS3_NORM_VPT 2
+#endif
+#ifndef ZS3_NORM_GRID
+#define ZS3_NORM_GRID 4096
+#endif
+#ifndef ZS3_ADAM_GPT
+#define ZS3_ADAM_GPT 1
+#endif
+#ifndef ZS3_ADAM_SUB
+#define ZS3_ADAM_SUB 4
+#endif
+// Non-temporal hints per family: on MI355X they help the copies, the
+// reduce-scatter and the norm, and slow the Adam pass (measured).
+#ifndef ZS3_NT_COPY
+#define ZS3_NT_COPY 1
+#endif
+#ifndef ZS3_NT_RS
+#define ZS3_NT_RS 1
+#endif
+#ifndef ZS3_NT_NORM
+#define ZS3_NT_NORM 1
+#endif
+#ifndef ZS3_NT_ADAM
+#define ZS3_NT_ADAM 0
+#endif
+
+constexpr int kCopyVPT = ZS3_COPY_VPT;
+constexpr int kCopySub = ZS3_COPY_SUB;
+constexpr int64_t kCopyPiece = int64_t(kBlock) * kCopyVPT * 8 * kCopySub;
+constexpr int kRsVPT = ZS3_RS_VPT;
+constexpr int kRsSub = ZS3_RS_SUB;
+constexpr int64_t kRsPiece = int64_t(kBlock) * kRsVPT * 8 * kRsSub;
+constexpr int kNormVPT = ZS3_NORM_VPT;     // vectors per thread per loop trip
+constexpr int kNormGrid = ZS3_NORM_GRID;   // workgroups of the sum-of-squares pass (upper bound)
+constexpr int kNormSub = 8;
+constexpr int64_t kNormPiece = int64_t(kBlock) * kNormVPT * 8 * kNormSub;
+constexpr int kAdamGPT = ZS3_ADAM_GPT;     // groups of 8 elements per thread
+constexpr int kAdamSub = ZS3_ADAM_SUB;
+constexpr int64_t kAdamPiece = int64_t(kBlock) * kAdamGPT * 8 * kAdamSub;
+constexpr bool kNtCopy = ZS3_NT_COPY != 0;
+constexpr bool kNtRs = ZS3_NT_RS != 0;
+constexpr bool kNtNorm = ZS3_NT_NORM != 0;
+constexpr bool kNtAdam = ZS3_NT_ADAM != 0;
 
 // A contiguous copy: dst[0 .. count) = src[0 .. count), or zeros if src is null.
 struct CopySeg {
@@ -62,7 +113,9 @@ struct AdamConsts {
 
 enum DType : int32_t { kFP16 = 1, kBF16 = 2 };
 
-enum CopyKind : int32_t { kCopyPartition = 1, kCopyPack = 2, kCopyUnpack = 3 };
+// kCopyGather: pack and unpack of one bucket in one launch (the unpack reads
+// the own rank's part from the shard, which is what the pack puts on the wire).
+enum CopyKind : int32_t { kCopyPartition = 1, kCopyPack = 2, kCopyUnpack = 3, kCopyGather = 4 };
 
 // ---- launchers (kernels.hip) -------------------------------------------
 hipError_t launch_copy(CopyKind kind, const CopySeg* segs, const Piece* pieces, int64_t n_pieces,
@@ -72,14 +125,14 @@ hipError_t launch_reduce_scatter(int32_t dtype, const RsSeg* segs, const Piece* 
                                  int64_t n_pieces, const uint16_t* const* srcs, int32_t world,
                                  bool co_aligned, hipStream_t stream);
 
-// Per-workgroup sums of squares of grad[span] (spans [0, n_part) partitioned,
-// [n_part, n_spans) persistent), then one workgroup combines them into
-// sumsq[rank], sumsq[world] and, if finalize, the norm, scale and flag.
-hipError_t launch_grad_norm(int32_t dtype, const uint16_t* grad, const Span* spans,
-                            int64_t n_spans, int64_t n_part, double* partials, double* sumsq,
-                            int32_t rank, int32_t world, int32_t finalize, double max_norm,
-                            double loss_scale, double* norm_out, float* scale_out,
-                            int32_t* nonfinite, hipStream_t stream);
+// Sums of squares of grad over the spans ([0, n_part) partitioned, the rest
+// persistent) by n_blocks workgroups into partials[2*n_blocks], then one
+// workgroup combines them into sumsq[rank], sumsq[world] and, if finalize,
+// the norm, scale and flag.
+hipError_t launch_grad_norm(int32_t dtype, const uint16_t* grad, const Span* spans, int64_t n_spans,
+                            int64_t n_part, int64_t n_blocks, double* partials, double* sumsq, int32_t rank,
+                            int32_t world, int32_t finalize, double max_norm, double loss_scale, double* norm_out,
+                            float* scale_out, int32_t* nonfinite, hipStream_t stream);
 
 hipError_t launch_adam(int32_t dtype, const Span* spans, int64_t n_spans, float* master,
                        float* exp_avg, float* exp_avg_sq, const uint16_t* grad, uint16_t* shard,

@@ -46,7 +46,7 @@ class ShardStep:
     def __init__(self, *, world_size: int, rank: int, threshold: int, ds_ids: Sequence[int],
                  numels: Sequence[int], dtype: str, prefetch_bucket_size: int, reduce_bucket_size: int,
                  sub_group_size: int, adam: AdamConfig = AdamConfig(), max_norm: float = 1.0,
-                 device: str = "cuda"):
+                 device: str = "cuda", rs_streams: int = 4):
         import torch
 
         self.torch = torch
@@ -102,6 +102,11 @@ class ShardStep:
         self.sumsq = torch.zeros(self.N + 1, dtype=torch.float64, device=dev)
         self.outs = torch.zeros(2, dtype=torch.float64, device=dev)   # norm | scale (f32), flag (i32)
         self.t = 0
+        # independent gradient buckets are spread over a few streams so that
+        # short reduce-scatter kernels overlap (default priority streams)
+        self.aux_streams = [torch.cuda.Stream(device=dev) for _ in range(max(0, rs_streams - 1))]
+        self._fork = torch.cuda.Event()
+        self._joins = [torch.cuda.Event() for _ in self.aux_streams]
         self._marshal()
 
     # ------------------------------------------------------------ pointers
@@ -159,6 +164,13 @@ class ShardStep:
         if st != 0:
             raise zs.Zs3Error(st, zs.zs3_last_error())
 
+    def gather(self, bi: int, stream=None):
+        """Pack + unpack of one bucket (one launch: the wire's own slot is the pack output)."""
+        n, ids, own, chunks, fullp = self._g[bi]
+        self._ok(zs.lib().zs3_gather_coalesced(self.h, self.rank, self.dcode, zs.ZS3_PACK | zs.ZS3_UNPACK, n, ids,
+                                               self.shard.data_ptr(), own, chunks, fullp, None,
+                                               stream if stream is not None else self._stream()))
+
     def pack(self, bi: int, stream=None):
         n, ids, own, chunks, fullp = self._g[bi]
         self._ok(zs.lib().zs3_gather_coalesced(self.h, self.rank, self.dcode, zs.ZS3_PACK, n, ids,
@@ -171,22 +183,29 @@ class ShardStep:
                                                chunks, fullp, None,
                                                stream if stream is not None else self._stream()))
 
-    def gather_pass(self, stream=None, on_unpack=None):
+    def gather_pass(self, stream=None):
         s = stream if stream is not None else self._stream()
         for bi in range(len(self._g)):
-            self.pack(bi, s)
-            if on_unpack is not None:
-                on_unpack(True)
-            self.unpack(bi, s)
-            if on_unpack is not None:
-                on_unpack(False)
+            self.gather(bi, s)
 
     def reduce_scatter(self, stream=None):
-        s = stream if stream is not None else self._stream()
+        """Every gradient bucket, fanned out over the main and auxiliary
+        streams and joined back into the main stream."""
+        torch = self.torch
+        main = torch.cuda.current_stream() if stream is None else stream
+        streams = [main] + self.aux_streams
+        if len(streams) > 1:
+            self._fork.record(main)
+            for a in self.aux_streams:
+                a.wait_event(self._fork)
+        handles = [int(x.cuda_stream) for x in streams]
         lib = zs.lib()
-        for n, ids, src in self._r:
+        for i, (n, ids, src) in enumerate(self._r):
             self._ok(lib.zs3_reduce_scatter_local(self.h, self.rank, self.dcode, n, ids, src,
-                                                  self.grad.data_ptr(), s))
+                                                  self.grad.data_ptr(), handles[i % len(handles)]))
+        for a, e in zip(self.aux_streams, self._joins):
+            e.record(a)
+            main.wait_event(e)
 
     def repartition(self, stream=None):
         n, ids, ptrs = self._p
@@ -208,15 +227,15 @@ class ShardStep:
                                             self.grad.data_ptr(), self.shard.data_ptr(), self.scale_ptr,
                                             self.flag_ptr, ctypes.byref(hp), s))
 
-    def step(self, stream=None, on_phase=None, on_unpack=None):
+    def step(self, stream=None, on_phase=None):
         """One whole shard step; ``on_phase(name)`` is called before each phase
         and with None at the end (for event timing)."""
         self.t += 1
         mark = on_phase or (lambda name: None)
         mark("gather_fwd")
-        self.gather_pass(stream, on_unpack)
+        self.gather_pass(stream)
         mark("gather_bwd")
-        self.gather_pass(stream, on_unpack)
+        self.gather_pass(stream)
         mark("reduce_scatter")
         self.reduce_scatter(stream)
         mark("partition")
