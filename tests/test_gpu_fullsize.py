@@ -1,0 +1,303 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration that
+bench.py times (ShardStep: per-bucket calls, fused gathers, gradient buckets
+over four streams).
+
+* c2 (GPT-2-small set) and c3 (one Llama-3-8B layer): the whole step chained
+  for 10 steps on the GPU against the oracle's own 10-step chain from the
+  same synthetic inputs (weights, per-step gradients, the peers' norm
+  partials); every output compared.
+* c4 (Llama-3-8B set, 8.03B parameters, rank 0) and c5 (ragged 7.46B set,
+  N = 64, rank 63, fp16, misaligned): each call fed fresh synthetic inputs,
+  its outputs checked on a sample of whole parameters (the oracle recomputes
+  those parameters only) or, for the norm, over the whole buffer.
+"""
+
+import gc
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import get_config
+from synth.gen import KIND_GRAD, KIND_STATE, KIND_WEIGHT, device_normal16, weights_host
+
+from gpu_util import assert_f32_close, note, ordinal16, require_gpu, sync
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    import torch
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _step(cfg, rank):
+    from zero_sharded_state_amd.shard_step import AdamConfig, ShardStep
+    return ShardStep(world_size=cfg.world_size, rank=rank, threshold=cfg.threshold, ds_ids=cfg.ds_ids,
+                     numels=cfg.numels, dtype=cfg.dtype, prefetch_bucket_size=cfg.prefetch_bucket_size,
+                     reduce_bucket_size=cfg.reduce_bucket_size, sub_group_size=cfg.sub_group_size,
+                     adam=AdamConfig(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay),
+                     max_norm=cfg.max_norm, rs_streams=4)
+
+
+def h16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def _hp(cfg, t):
+    return oracle.AdamHParams(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, t)
+
+
+def _recv_grads(step, L, host_recv):
+    """Oracle-side gradients: virtual rank v's full gradient of every
+    parameter, zero except the slice this rank receives (the oracle reads
+    only that slice)."""
+    N, S = step.N, step.S
+    grads = []
+    for v in range(N):
+        g = {}
+        for p in L.params:
+            lo, hi = L.own_range(p, step.rank)
+            a = np.zeros(p.numel, np.uint16)
+            o = v * S + p.shard_offset
+            a[lo:hi] = host_recv[o:o + (hi - lo)]
+            g[p.ds_id] = a
+        grads.append(g)
+    return grads
+
+
+# --------------------------------------------------------------------------
+# c2 / c3: the whole step, chained, 10 steps
+# --------------------------------------------------------------------------
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,rank", [("c2", 0), ("c2", 7), ("c3", 0), ("c3", 7)])
+def test_chained_steps_match_oracle(name, rank):
+    import torch
+    cfg = get_config(name)
+    N, dt = cfg.world_size, cfg.dtype
+    note(f"chain {name} rank={rank}: set-up")
+    step = _step(cfg, rank)
+    L = oracle.make_layout(N, cfg.threshold, cfg.ds_ids, cfg.numels)
+    try:
+        full = {d: weights_host(cfg, d) for d in cfg.ds_ids}
+        for d in cfg.ds_ids:
+            p = step.by_id[d]
+            if p["persistent"]:
+                o = step.pers_off[d]
+                step.pers_full[o:o + p["numel"]].copy_(torch.from_numpy(full[d].view(np.int16)))
+            else:
+                o = step.full_off[d]
+                step.full[o:o + p["numel"]].copy_(torch.from_numpy(full[d].view(np.int16)))
+        step.init_from_full()
+        # oracle: every rank's shard and every bucket's chunks, this rank's fp32 state
+        shards = [oracle.partition(L, v, full) for v in range(N)]
+        chunks = {tuple(b): [oracle.pack(L, v, b, shards[v]) for v in range(N)] for b in step.gather_buckets}
+        shard = shards[rank].copy()
+        w, m, v_ = oracle.init_state(shard, dt)
+        peers = np.random.default_rng(cfg.config_id).uniform(0.5, 2.0, N) * 1e-3   # what the all-reduce delivers
+        for t in range(1, cfg.steps + 1):
+            note(f"chain {name} rank={rank}: step {t}")
+            device_normal16(step.N * step.S, cfg.grad_std, dt, step.device, (cfg.seed, cfg.config_id, KIND_GRAD, t),
+                            outlier_prob=cfg.outlier_prob, outlier_mult=cfg.outlier_mult, out=step.recv)
+            host_recv = h16(step.recv)
+            # GPU: the step as bench.py runs it, with the peers' partial sums supplied
+            step.t = t - 1
+            step.gather_pass()
+            step.gather_pass()
+            step.reduce_scatter()
+            step.repartition()
+            step.sumsq.copy_(torch.from_numpy(np.append(peers, 0.0)))
+            step.grad_norm()
+            step.adam_step(t)
+            step.t = t
+            # oracle chain
+            gf = np.zeros(L.shard_numel, np.uint16)
+            grads = _recv_grads(step, L, host_recv)
+            for b in oracle.reduce_buckets(L, cfg.reduce_bucket_size):
+                oracle.reduce_scatter(L, rank, dt, b, grads, gf)
+            a, q = oracle.grad_norm_partial(L, rank, dt, gf)
+            parts = list(peers)
+            parts[rank] = a
+            norm, coef, scale, bad = oracle.grad_norm_finalize(parts, q, cfg.max_norm)
+            shard_before = shard.copy()
+            for b, e in oracle.sub_groups(L, cfg.sub_group_size):
+                oracle.adam_step(L, rank, dt, b, e, w, m, v_, gf, shard, scale, bad, _hp(cfg, t))
+            sync()
+            assert np.array_equal(h16(step.grad), gf), f"reduce-scatter differs at step {t}"
+            o = step.outs.cpu().numpy()
+            assert abs(float(o[0]) - norm) <= 1e-5 * norm
+            assert int(o[1:2].view(np.int32)[1]) == int(bad)
+        # gathered parameters of the last step = the oracle's gather of the shard it started from
+        got_full = h16(step.full)
+        for bi, b in enumerate(step.gather_buckets):
+            ch = list(chunks[tuple(b)])
+            ch[rank] = oracle.pack(L, rank, b, shard_before)
+            ref, offs = oracle.unpack(L, b, ch)
+            fo, fn, _, _ = step.bucket_meta[bi]
+            assert np.array_equal(got_full[fo:fo + fn], ref), f"bucket {bi} gathered parameters differ"
+        for nm, got, ref in (("master", step.master, w), ("exp_avg", step.exp_avg, m),
+                             ("exp_avg_sq", step.exp_avg_sq, v_)):
+            assert_f32_close(got.cpu().numpy(), ref, 2e-6, nm)
+        d = np.abs(ordinal16(h16(step.shard)) - ordinal16(shard))
+        assert d.max() <= 1
+    finally:
+        step.destroy()
+        del step
+
+
+# --------------------------------------------------------------------------
+# c4 / c5: every call at full size, sampled parameters
+# --------------------------------------------------------------------------
+
+def _sample_params(L, cfg, k=6):
+    """A deterministic sample: the largest partitioned parameter, the last
+    one, a persistent one, and a few spread over the ds_id range."""
+    part = [p for p in L.params if not p.persistent]
+    pers = [p for p in L.params if p.persistent]
+    pick = {max(part, key=lambda p: p.numel).ds_id, part[-1].ds_id}
+    if pers:
+        pick.add(pers[len(pers) // 2].ds_id)
+    idx = np.linspace(0, len(L.params) - 1, k).astype(int)
+    pick |= {L.params[i].ds_id for i in idx}
+    return sorted(pick)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["c4", "c5"])
+def test_fullsize_calls_on_sampled_parameters(name):
+    import torch
+    cfg = get_config(name)
+    rank = cfg.bench_rank
+    N, dt = cfg.world_size, cfg.dtype
+    note(f"fullsize {name} rank={rank}: set-up")
+    step = _step(cfg, rank)
+    L = oracle.make_layout(N, cfg.threshold, cfg.ds_ids, cfg.numels)
+    sample = _sample_params(L, cfg)
+    dev = step.device
+    try:
+        # ---- partition: synthetic full parameters -> shard
+        device_normal16(step.F, cfg.weight_std, dt, dev, (cfg.seed, cfg.config_id, KIND_WEIGHT, 0), out=step.full)
+        device_normal16(step.P, cfg.weight_std, dt, dev, (cfg.seed, cfg.config_id, KIND_WEIGHT, 1), out=step.pers_full)
+        note(f"fullsize {name}: partition")
+        step.repartition()
+        sync()
+        got = h16(step.shard)
+        for d in sample:
+            p = L.slot(d)
+            if p.persistent:
+                o = step.pers_off[d]
+                src = h16(step.pers_full[o:o + p.numel])
+            else:
+                o = step.full_off[d]
+                src = h16(step.full[o:o + p.numel])
+            sub = oracle.make_layout(N, cfg.threshold, [d], [p.numel])
+            ref = oracle.partition(sub, rank, {d: src})
+            assert np.array_equal(got[p.shard_offset:p.shard_offset + p.partition_size], ref), f"partition {d}"
+
+        # ---- gather: synthetic shard and wire -> own chunks and full parameters
+        device_normal16(step.S, cfg.weight_std, dt, dev, (cfg.seed, cfg.config_id, KIND_WEIGHT, 2), out=step.shard)
+        device_normal16(step.W, cfg.weight_std, dt, dev, (cfg.seed, cfg.config_id, KIND_WEIGHT, 3), out=step.wire)
+        sb = {bi for bi, b in enumerate(step.gather_buckets) if set(b) & set(sample)}
+        wire_before = {bi: h16(step.wire[step.bucket_meta[bi][2]:step.bucket_meta[bi][2] +
+                                         N * step.bucket_meta[bi][3]]) for bi in sb}
+        note(f"fullsize {name}: gather pass")
+        step.gather_pass()
+        sync()
+        shard_h = h16(step.shard)
+        full_h = h16(step.full)
+        for bi in sorted(sb):
+            b = step.gather_buckets[bi]
+            fo, fn, wo, cn = step.bucket_meta[bi]
+            ch = [wire_before[bi][v * cn:(v + 1) * cn] for v in range(N)]
+            ch[rank] = oracle.pack(L, rank, b, shard_h)
+            ref, _ = oracle.unpack(L, b, ch)
+            assert np.array_equal(full_h[fo:fo + fn], ref), f"gathered bucket {bi}"
+            own = h16(step.wire[wo + rank * cn:wo + (rank + 1) * cn])
+            assert np.array_equal(own, ch[rank]), f"packed chunk of bucket {bi}"
+
+        # ---- reduce-scatter: synthetic received slices -> flat gradient
+        device_normal16(step.N * step.S, cfg.grad_std, dt, dev, (cfg.seed, cfg.config_id, KIND_GRAD, 1),
+                        outlier_prob=cfg.outlier_prob, outlier_mult=cfg.outlier_mult, out=step.recv)
+        note(f"fullsize {name}: reduce-scatter")
+        step.grad.fill_(0x3C3C)
+        step.reduce_scatter()
+        sync()
+        gh = h16(step.grad)
+        for d in sample:
+            p = L.slot(d)
+            lo, hi = L.own_range(p, rank)
+            grads = []
+            for v in range(N):
+                a = np.zeros(p.numel, np.uint16)
+                o = v * step.S + p.shard_offset
+                a[lo:hi] = h16(step.recv[o:o + (hi - lo)])
+                grads.append({d: a})
+            sub = oracle.make_layout(N, cfg.threshold, [d], [p.numel])
+            ref = np.zeros(sub.shard_numel, np.uint16)
+            oracle.reduce_scatter(sub, rank, dt, [d], grads, ref)
+            assert np.array_equal(gh[p.shard_offset:p.shard_offset + p.partition_size], ref), f"reduce-scatter {d}"
+
+        # ---- norm: synthetic flat gradient (padding zero) -> partial sums, norm, scale
+        device_normal16(step.S, 1e-3, dt, dev, (cfg.seed, cfg.config_id, KIND_GRAD, 2), out=step.grad)
+        pad = oracle.padding_mask(L, rank)
+        if pad.any():
+            step.grad[torch.from_numpy(pad).to(dev)] = 0
+        peers = np.random.default_rng(5).uniform(0.5, 2.0, N)
+        step.sumsq.copy_(torch.from_numpy(np.append(peers, 0.0)))
+        note(f"fullsize {name}: grad norm")
+        step.grad_norm()
+        sync()
+        gflat = h16(step.grad)
+        a, q = oracle.grad_norm_partial(L, rank, dt, gflat)
+        parts = list(peers)
+        parts[rank] = a
+        norm, coef, scale, bad = oracle.grad_norm_finalize(parts, q, cfg.max_norm)
+        s = step.sumsq.cpu().numpy()
+        assert s[rank] == pytest.approx(a, rel=1e-10) and s[N] == pytest.approx(q, rel=1e-10, abs=1e-300)
+        o = step.outs.cpu().numpy()
+        assert abs(float(o[0]) - norm) <= 1e-5 * norm
+        gscale = float(o[1:2].view(np.float32)[0])
+        assert abs(gscale - float(scale)) <= np.spacing(np.float32(scale))
+
+        # ---- Adam: synthetic master, 10 steps of synthetic gradients, the GPU's scale
+        device_normal16(step.S, 1.0, "bf16", dev, (cfg.seed, cfg.config_id, KIND_STATE, 0), out=step.grad)
+        step.master.copy_(step.grad.view(torch.bfloat16).to(torch.float32) * 0.02)
+        step.exp_avg.zero_()
+        step.exp_avg_sq.zero_()
+        w0 = {d: step.master[L.slot(d).shard_offset:L.slot(d).shard_offset + L.slot(d).partition_size].cpu().numpy()
+              for d in sample}
+        gs = {d: [] for d in sample}
+        for t in range(1, 11):
+            device_normal16(step.S, 1e-3, dt, dev, (cfg.seed, cfg.config_id, KIND_GRAD, 10 + t), out=step.grad)
+            for d in sample:
+                p = L.slot(d)
+                gs[d].append(h16(step.grad[p.shard_offset:p.shard_offset + p.partition_size]))
+            note(f"fullsize {name}: adam step {t}")
+            step.adam_step(t)
+        sync()
+        sc = np.float32(gscale)
+        for d in sample:
+            p = L.slot(d)
+            sub = oracle.make_layout(N, cfg.threshold, [d], [p.numel])
+            w = w0[d].copy()
+            m = np.zeros_like(w)
+            v = np.zeros_like(w)
+            sh = np.zeros(p.partition_size, np.uint16)
+            for t in range(1, 11):
+                oracle.adam_step(sub, rank, dt, 0, sub.shard_numel, w, m, v, gs[d][t - 1], sh, sc, False, _hp(cfg, t))
+            o0, o1 = p.shard_offset, p.shard_offset + p.partition_size
+            real = ~oracle.padding_mask(sub, rank)
+            for nm, got, ref in (("master", step.master[o0:o1], w), ("exp_avg", step.exp_avg[o0:o1], m),
+                                 ("exp_avg_sq", step.exp_avg_sq[o0:o1], v)):
+                gg = got.cpu().numpy()
+                assert_f32_close(gg[real], ref[real], 2e-6, f"{nm} of {d}")
+            dd = np.abs(ordinal16(h16(step.shard[o0:o1])[real]) - ordinal16(sh[real]))
+            assert dd.max() <= 1, f"shard of {d}"
+    finally:
+        step.destroy()
+        del step

@@ -323,3 +323,123 @@ def test_adam_nonfinite_flag_skips_everything():
         assert np.array_equal(W.host(), w) and np.all(M.host() == 0) and np.all(V.host() == 0)
     finally:
         zs.zs3_layout_destroy(h)
+
+
+# ------------------------------------------------------------- edge cases
+
+def test_empty_requests_are_noops():
+    h = zs.zs3_layout_create(4, 0, [0, 1], [10, 20])
+    try:
+        out = Buf16(8)
+        zs.zs3_partition(h, 0, "bf16", [], [], out.ptr())
+        assert zs.zs3_gather_coalesced(h, 0, "bf16", zs.ZS3_PACK | zs.ZS3_UNPACK, [], out.ptr(), out.ptr(),
+                                       [out.ptr()] * 4, out.ptr()) == []
+        zs.zs3_reduce_scatter_local(h, 0, "bf16", [], [], out.ptr())
+        import torch
+        st = torch.zeros(4, dtype=torch.float32, device="cuda")
+        zs.zs3_adam_step(h, 0, "bf16", 3, 3, st.data_ptr(), st.data_ptr(), st.data_ptr(), out.ptr(), out.ptr(),
+                         st.data_ptr(), None, oracle.AdamHParams(step=1))
+        sync()
+        out.check_guards()
+    finally:
+        zs.zs3_layout_destroy(h)
+
+
+def test_empty_layout_norm_is_zero():
+    import torch
+    h = zs.zs3_layout_create(2, 0, [], [])
+    try:
+        sumsq = torch.full((3,), 7.0, dtype=torch.float64, device="cuda")
+        outs = torch.zeros(2, dtype=torch.float64, device="cuda")
+        g = Buf16(1)
+        sumsq[1] = 4.0
+        zs.zs3_grad_norm(h, 0, "fp16", g.ptr(), sumsq, True, 1.0, 1.0, outs.data_ptr(), outs.data_ptr() + 8,
+                         outs.data_ptr() + 12)
+        sync()
+        s = sumsq.cpu().numpy()
+        assert s[0] == 0.0 and s[2] == 0.0 and float(outs.cpu().numpy()[0]) == 2.0
+    finally:
+        zs.zs3_layout_destroy(h)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_ranks_holding_only_padding(dtype):
+    """numel 3 over N = 8: ranks 3..7 hold only padding, and 1-element
+    parameters leave every rank but 0 empty."""
+    N = 8
+    ids, numels = [0, 1, 2], [3, 1, 17]
+    h, L = _layout(ids, numels, N, 0)
+    try:
+        full = {d: random_bits16(d, n, dtype, 0.5, 3) for d, n in zip(ids, numels)}
+        srcs = {d: Buf16(numels[i], fill=full[d]) for i, d in enumerate(ids)}
+        grads = [{d: random_bits16(10 + v, n, dtype, 0.1, d) for d, n in zip(ids, numels)} for v in range(N)]
+        gbufs = [{d: Buf16(numels[i], fill=grads[v][d]) for i, d in enumerate(ids)} for v in range(N)]
+        for r in range(N):
+            note(f"padding-only ranks {dtype} rank={r}")
+            sh = Buf16(L.shard_numel, fill=np.full(L.shard_numel, 0x1111, np.uint16))
+            zs.zs3_partition(h, r, dtype, ids, [srcs[d].ptr() for d in ids], sh.ptr())
+            gf = Buf16(L.shard_numel, fill=np.full(L.shard_numel, 0x2222, np.uint16))
+            src = []
+            for d in ids:
+                lo, hi = L.own_range(L.slot(d), r)
+                src += [gbufs[v][d].ptr() + 2 * lo if hi > lo else 0 for v in range(N)]
+            zs.zs3_reduce_scatter_local(h, r, dtype, ids, src, gf.ptr())
+            sync()
+            assert np.array_equal(sh.host(), oracle.partition(L, r, full))
+            ref = np.zeros(L.shard_numel, np.uint16)
+            oracle.reduce_scatter(L, r, dtype, ids, grads, ref)
+            assert np.array_equal(gf.host(), ref)
+            sh.check_guards()
+            gf.check_guards()
+    finally:
+        zs.zs3_layout_destroy(h)
+
+
+def test_fp16_overflow_sets_flag_and_adam_skips():
+    """Averaging fp16 gradients near the top of the range still fits, but a
+    gradient of inf makes the norm non-finite and the step is skipped."""
+    import torch
+    N = 4
+    h = zs.zs3_layout_create(N, 0, [0], [4096])
+    try:
+        g = np.full(4096, 0x7BFF, np.uint16)           # 65504, the largest fp16
+        g[100] = 0x7C00                                  # +inf
+        bufs = [Buf16(4096, fill=g) for _ in range(N)]
+        gf = Buf16(1024)
+        zs.zs3_reduce_scatter_local(h, 0, "fp16", [0], [b.ptr() for b in bufs], gf.ptr())
+        ref = np.zeros(1024, np.uint16)
+        oracle.reduce_scatter(oracle.make_layout(N, 0, [0], [4096]), 0, "fp16", [0], [{0: g}] * N, ref)
+        sync()
+        assert np.array_equal(gf.host(), ref)
+        assert gf.host()[0] == 0x7BFF and gf.host()[100] == 0x7C00
+        sumsq = torch.zeros(N + 1, dtype=torch.float64, device="cuda")
+        outs = torch.zeros(2, dtype=torch.float64, device="cuda")
+        zs.zs3_grad_norm(h, 0, "fp16", gf.ptr(), sumsq, True, 1.0, 1.0, outs.data_ptr(), outs.data_ptr() + 8,
+                         outs.data_ptr() + 12)
+        W = Buf32(1024, 0, np.ones(1024, np.float32))
+        M, V = Buf32(1024, 0, np.zeros(1024, np.float32)), Buf32(1024, 0, np.zeros(1024, np.float32))
+        S = Buf16(1024, 0, np.full(1024, 0x3C00, np.uint16))
+        zs.zs3_adam_step(h, 0, "fp16", 0, 1024, W.ptr(), M.ptr(), V.ptr(), gf.ptr(), S.ptr(), outs.data_ptr() + 8,
+                         outs.data_ptr() + 12, oracle.AdamHParams(step=1))
+        sync()
+        assert int(outs.cpu().numpy()[1:2].view(np.int32)[1]) == 1
+        assert np.all(W.host() == 1.0) and np.all(M.host() == 0) and np.all(S.host() == 0x3C00)
+    finally:
+        zs.zs3_layout_destroy(h)
+
+
+def test_repeated_calls_reuse_plans_and_stay_exact():
+    """The second and third identical calls take the cached work list."""
+    seed, N, T, n, mx = PROBLEMS[4]
+    ids, numels, full = _problem(seed, N, T, n, mx)
+    h, L = _layout(ids, numels, N, T)
+    try:
+        srcs = {d: Buf16(full[d].size, fill=full[d]) for d in ids}
+        ref = oracle.partition(L, 3, full)
+        for k in range(3):
+            out = Buf16(L.shard_numel)
+            zs.zs3_partition(h, 3, "bf16", ids, [srcs[d].ptr() for d in ids], out.ptr())
+            sync()
+            assert np.array_equal(out.host(), ref)
+    finally:
+        zs.zs3_layout_destroy(h)
