@@ -46,7 +46,9 @@ def parse():
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=12, help="decoder layers in the oracle's sample")
-    ap.add_argument("--rs-streams", type=int, default=4, help="streams the gradient buckets are spread over")
+    ap.add_argument("--rs-streams", type=int, default=1, help="streams the gradient buckets are spread over")
+    ap.add_argument("--gather-streams", type=int, default=1, help="streams the gather buckets are spread over")
+    ap.add_argument("--no-kernel-timer", action="store_true", help="do not time the gather launches")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -73,14 +75,50 @@ def traffic_entry(config: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def make_step(cfg, rank, rs_streams=4):
+class KernelTimer:
+    """Pre-created hipEvent_t pairs handed out one per timed launch; each
+    launch records its own start and end timestamps into its pair."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")     # the runtime already loaded by torch and libzs3
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(a)) or self.hip.hipEventCreate(ctypes.byref(b)):
+                raise RuntimeError("hipEventCreate failed")
+            self.pairs.append((a.value, b.value))
+        self.used = 0
+
+    def __call__(self):
+        p = self.pairs[self.used]
+        self.used += 1
+        return p
+
+    def durations_ms(self):
+        out = []
+        ms = self.ct.c_float()
+        for a, b in self.pairs[:self.used]:
+            if self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ct.c_void_p(a), self.ct.c_void_p(b)):
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(self.ct.c_void_p(a))
+            self.hip.hipEventDestroy(self.ct.c_void_p(b))
+
+
+def make_step(cfg, rank, rs_streams=1, gather_streams=1):
     from zero_sharded_state_amd.shard_step import AdamConfig, ShardStep
 
     return ShardStep(world_size=cfg.world_size, rank=rank, threshold=cfg.threshold, ds_ids=cfg.ds_ids,
                      numels=cfg.numels, dtype=cfg.dtype, prefetch_bucket_size=cfg.prefetch_bucket_size,
                      reduce_bucket_size=cfg.reduce_bucket_size, sub_group_size=cfg.sub_group_size,
                      adam=AdamConfig(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay),
-                     max_norm=cfg.max_norm, rs_streams=rs_streams)
+                     max_norm=cfg.max_norm, rs_streams=rs_streams, gather_streams=gather_streams)
 
 
 def fill_inputs(step, cfg):
@@ -206,7 +244,7 @@ def main():
     cfg = get_config(args.config)
     rank = cfg.bench_rank if args.rank is None else args.rank
     log(f"config {cfg.name}: {cfg.title}, rank {rank}")
-    step = make_step(cfg, rank, args.rs_streams)
+    step = make_step(cfg, rank, args.rs_streams, args.gather_streams)
     log(f"layout: S+P={step.S:,} own real={step.own_real:,} F={step.F:,} gather buckets={len(step.gather_buckets)} "
         f"reduce buckets={len(step.reduce_buckets)} sub-groups={len(step.sub_groups)}")
     t0 = time.time()
@@ -228,11 +266,17 @@ def main():
         e.record(stream)
         phase_events[-1].append((name, e))
 
+    # One gather stream: launches run back to back, so the gather phases'
+    # event time over the launch count is the average kernel duration (it
+    # matches rocprofv3's).  Several streams overlap launches: then every
+    # launch records its own start/end (this costs a few us per launch).
+    per_launch = step.gather_streams > 1 and not args.no_kernel_timer
+    timer = KernelTimer(2 * len(step.gather_buckets) * args.steps if per_launch else 0)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(args.steps):
         phase_events.append([])
-        step.step(on_phase=on_phase)
+        step.step(on_phase=on_phase, gather_timer=timer if per_launch else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     log(f"timed {args.steps} steps in {wall:.3f} s")
@@ -252,6 +296,9 @@ def main():
                    "gather_bwd": (nbytes["pack"] + nbytes["unpack"]) // 2,
                    "reduce_scatter": nbytes["reduce_scatter"], "partition": nbytes["partition"],
                    "grad_norm": nbytes["grad_norm"], "adam": nbytes["adam"]}
+    per_step = sorted(evs[0][1].elapsed_time(evs[-1][1]) for evs in phase_events)
+    step_stats = {"min": round(per_step[0], 4), "median": round(per_step[len(per_step) // 2], 4),
+                  "max": round(per_step[-1], 4)}
     kernels = {}
     for name, ms in phases.items():
         ms /= args.steps
@@ -259,20 +306,23 @@ def main():
                          "GBps": round(phase_bytes[name] / (ms * 1e-3) / 1e9, 1)}
 
     # Roofline entry of the dominant kernel: the fused gather (pack + unpack
-    # of one bucket, k_copy<4>), launched back to back on one stream in the
-    # two gather phases; its average launch duration is the phases' event
-    # time over the launch count.
+    # of one bucket, k_copy<4>), average duration over the timed launches.
     launches = 2 * len(step.gather_buckets) * args.steps
-    gather_ms = sum(phases.get(k, 0.0) for k in ("gather_fwd", "gather_bwd"))
+    if per_launch:
+        durs = timer.durations_ms()
+        avg_ms = sum(durs) / len(durs)
+    else:
+        avg_ms = sum(phases.get(k, 0.0) for k in ("gather_fwd", "gather_bwd")) / launches
+    timer.close()
     gather_bytes = nbytes["pack"] + nbytes["unpack"]
     per_launch_bytes = gather_bytes / (2 * len(step.gather_buckets))
-    avg_ms = gather_ms / launches
     achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
     roofline = {"kernel": "gather: pack + unpack of one bucket (k_copy<4>)", "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_entry(cfg.name),
                 "launches": launches, "avg_launch_ms": round(avg_ms, 5),
-                "algorithmic_bytes_per_launch": int(per_launch_bytes)}
+                "algorithmic_bytes_per_launch": int(per_launch_bytes),
+                "streams": step.gather_streams}
 
     if args.calibrate_copy_gib > 0:
         n = int(args.calibrate_copy_gib * 2**30) // 2
@@ -296,6 +346,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms_events": step_stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -94,6 +94,14 @@ ZS3_API const char* zs3_status_str(zs3_status s);
 /* Message of the last failed call on this host thread ("" if none). */
 ZS3_API const char* zs3_last_error(void);
 
+/* Instrumentation (for callers that measure kernels, not part of the method):
+ * the next kernel this host thread launches through any zs3 call records its
+ * own start and end timestamps into start_event / stop_event (hipEvent_t,
+ * created by the caller, either may be NULL), as hipExtLaunchKernel does; no
+ * extra commands are enqueued.  The setting applies to exactly one launch
+ * (calls that launch two kernels time the first).  Always returns ZS3_OK. */
+ZS3_API zs3_status zs3_time_next_launch(void* start_event, void* stop_event);
+
 /* ------------------------------------------------------------- layout
  * [codex] 3.1: rank r holds elements [r*partition_size, (r+1)*partition_size)
  * of every flattened parameter.  [codex] 5.3: parameters with

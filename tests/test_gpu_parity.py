@@ -443,3 +443,25 @@ def test_repeated_calls_reuse_plans_and_stay_exact():
             assert np.array_equal(out.host(), ref)
     finally:
         zs.zs3_layout_destroy(h)
+
+
+def test_time_next_launch_records_kernel_timestamps():
+    """The instrumentation hook times exactly the next launch."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    a, b = ctypes.c_void_p(), ctypes.c_void_p()
+    assert hip.hipEventCreate(ctypes.byref(a)) == 0 and hip.hipEventCreate(ctypes.byref(b)) == 0
+    h = zs.zs3_layout_create(1, 0, [0], [1 << 24])
+    try:
+        src, dst = Buf16(1 << 24), Buf16(1 << 24)
+        zs.zs3_time_next_launch(a.value, b.value)
+        zs.zs3_partition(h, 0, "bf16", [0], [src.ptr()], dst.ptr())
+        zs.zs3_partition(h, 0, "bf16", [0], [src.ptr()], dst.ptr())     # not timed
+        sync()
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        assert 0.0 < ms.value < 50.0
+    finally:
+        zs.zs3_layout_destroy(h)
+        hip.hipEventDestroy(a)
+        hip.hipEventDestroy(b)

@@ -38,7 +38,7 @@ DTYPES = {"fp16": ZS3_FP16, "bf16": ZS3_BF16}
 
 # Every exported symbol of include/zs3.h.
 EXPORTS = (
-    "zs3_abi_version", "zs3_status_str", "zs3_last_error",
+    "zs3_abi_version", "zs3_status_str", "zs3_last_error", "zs3_time_next_launch",
     "zs3_layout_create", "zs3_layout_destroy", "zs3_layout_info", "zs3_layout_param_at",
     "zs3_layout_param", "zs3_layout_own_range", "zs3_plan_buckets", "zs3_sub_groups",
     "zs3_bucket_sizes", "zs3_partition", "zs3_gather_coalesced", "zs3_reduce_scatter_local",
@@ -74,6 +74,7 @@ _SIGNATURES = {
     "zs3_abi_version": (_c_i32, []),
     "zs3_status_str": (ctypes.c_char_p, [_c_i32]),
     "zs3_last_error": (ctypes.c_char_p, []),
+    "zs3_time_next_launch": (_c_i32, [_c_p, _c_p]),
     "zs3_layout_create": (_c_i32, [_c_i32, _c_i64, _c_i32, _p_i64, _p_i64, ctypes.POINTER(_c_p)]),
     "zs3_layout_destroy": (None, [_c_p]),
     "zs3_layout_info": (_c_i32, [_c_p, _p_i32, _p_i64, _p_i32, _p_i64, _p_i64]),
@@ -170,6 +171,12 @@ def zs3_status_str(status: int) -> str:
 
 def zs3_last_error() -> str:
     return lib().zs3_last_error().decode(errors="replace")
+
+
+def zs3_time_next_launch(start_event, stop_event) -> None:
+    """The calling thread's next zs3 kernel launch records its start/end
+    timestamps into these hipEvent_t handles (integers)."""
+    _check(lib().zs3_time_next_launch(start_event, stop_event))
 
 
 def zs3_layout_create(world_size: int, persistence_threshold: int, ds_ids: Sequence[int],

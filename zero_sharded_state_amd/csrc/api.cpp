@@ -102,6 +102,10 @@ struct Plan {
     bool co_aligned = true;       // reduce-scatter: every source co-aligned with its dst
     size_t off_segs = 0, off_pieces = 0, off_srcs = 0, off_scratch = 0;
 
+    std::shared_ptr<CopyInline> copy_inline;   // set: the plan travels in the kernel arguments
+    std::shared_ptr<RsInline> rs_inline;
+    std::shared_ptr<AdamInline> adam_inline;
+
     template <typename T>
     T* at(size_t off) const { return reinterpret_cast<T*>(static_cast<char*>(dev) + off); }
 };
@@ -267,7 +271,7 @@ zs3_status build_copy_plan(zs3_layout* L, Key&& key, const std::vector<CopySeg>&
     std::vector<CopySeg> segs;
     for (const CopySeg& s : segs_in) {
         if (s.count <= 0) continue;
-        if (!segs.empty()) {
+        if (!segs.empty() && segs.back().dst2 == nullptr && s.dst2 == nullptr) {
             CopySeg& b = segs.back();
             const bool dst_next = b.dst + b.count == s.dst;
             const bool src_next = (b.src == nullptr && s.src == nullptr) ||
@@ -284,6 +288,29 @@ zs3_status build_copy_plan(zs3_layout* L, Key&& key, const std::vector<CopySeg>&
         add_pieces(&pieces, static_cast<int32_t>(i), reinterpret_cast<uintptr_t>(segs[i].dst), segs[i].count, kCopyPiece);
     zs3_status s = check_grid(static_cast<int64_t>(pieces.size()), kCopySub);
     if (s != ZS3_OK) return s;
+    if (segs.size() <= static_cast<size_t>(kCopyInlineSegs)) {
+        auto ci = std::make_shared<CopyInline>();
+        std::memset(ci.get(), 0, sizeof(CopyInline));
+        ci->nseg = static_cast<int32_t>(segs.size());
+        std::vector<int32_t> per_seg(segs.size(), 0);
+        for (const Piece& pc : pieces) ++per_seg[pc.seg];
+        int32_t np = 0;
+        for (size_t i = 0; i < segs.size(); ++i) {
+            ci->piece_start[i] = np;
+            np += per_seg[i];
+            ci->head[i] = static_cast<int32_t>(((16u - (reinterpret_cast<uintptr_t>(segs[i].dst) & 15u)) & 15u) >> 1);
+            ci->src[i] = segs[i].src;
+            ci->dst[i] = segs[i].dst;
+            ci->count[i] = segs[i].count;
+            ci->dst2[i] = segs[i].dst2;
+            ci->count2[i] = segs[i].count2;
+        }
+        ci->piece_start[segs.size()] = np;
+        Plan plan;
+        plan.n_pieces = np;
+        plan.copy_inline = std::move(ci);
+        return store_plan(L, std::move(key), std::move(plan), out);
+    }
     Plan plan;
     plan.n_pieces = static_cast<int64_t>(pieces.size());
     std::vector<size_t> offs;
@@ -296,6 +323,9 @@ zs3_status build_copy_plan(zs3_layout* L, Key&& key, const std::vector<CopySeg>&
 }
 
 zs3_status run_copy(CopyKind kind, const Plan* p, void* stream) {
+    if (p->copy_inline)
+        return hip_status(launch_copy_inline(kind, *p->copy_inline, static_cast<hipStream_t>(stream)),
+                          "copy kernel launch");
     return hip_status(launch_copy(kind, p->at<CopySeg>(p->off_segs), p->at<Piece>(p->off_pieces), p->n_pieces,
                                   static_cast<hipStream_t>(stream)),
                       "copy kernel launch");
@@ -332,6 +362,11 @@ const char* zs3_status_str(zs3_status s) {
 }
 
 const char* zs3_last_error(void) { return g_last_error.c_str(); }
+
+zs3_status zs3_time_next_launch(void* start_event, void* stop_event) {
+    set_launch_events(static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
+    return ok();
+}
 
 zs3_status zs3_layout_create(int32_t world_size, int64_t persistence_threshold, int32_t n_params,
                              const int64_t* ds_id, const int64_t* numel, zs3_layout_t* out) {
@@ -526,8 +561,8 @@ zs3_status zs3_partition(zs3_layout_t L, int32_t rank, int32_t dtype, int32_t n,
             int64_t lo, hi;
             p.own_range(rank, &lo, &hi);
             const uint16_t* src = static_cast<const uint16_t*>(full_params[k]);
-            segs.push_back(CopySeg{src + lo, base + p.offset, hi - lo, 0});
-            segs.push_back(CopySeg{nullptr, base + p.offset + (hi - lo), p.ps - (hi - lo), 0});
+            segs.push_back(CopySeg{src + lo, base + p.offset, hi - lo, nullptr, 0});
+            segs.push_back(CopySeg{nullptr, base + p.offset + (hi - lo), p.ps - (hi - lo), nullptr, 0});
         }
         if ((s = build_copy_plan(L, std::move(key), segs, &plan)) != ZS3_OK) return s;
     }
@@ -594,16 +629,27 @@ zs3_status zs3_gather_coalesced(zs3_layout_t L, int32_t rank, int32_t dtype, int
             uint16_t* dst = static_cast<uint16_t*>(full_flat);
             for (int32_t k : order) {
                 const Slot& p = L->params[pos[k]];
-                segs.push_back(CopySeg{shard + p.offset, own + c[k], p.ps, 0});
+                int64_t lo, hi;
+                p.own_range(rank, &lo, &hi);
+                uint16_t* own_dst = own + c[k];
+                uint16_t* full_dst = dst + f[k] + lo;
+                // read the own shard once for both destinations when they are co-aligned
+                const bool both = hi > lo && ((reinterpret_cast<uintptr_t>(own_dst) ^ reinterpret_cast<uintptr_t>(full_dst)) & 15u) == 0;
+                if (both) {
+                    segs.push_back(CopySeg{shard + p.offset, own_dst, p.ps, full_dst, hi - lo});
+                } else {
+                    segs.push_back(CopySeg{shard + p.offset, own_dst, p.ps, nullptr, 0});
+                    segs.push_back(CopySeg{shard + p.offset, full_dst, hi - lo, nullptr, 0});
+                }
             }
             for (int32_t k : order) {
                 const Slot& p = L->params[pos[k]];
                 for (int32_t v = 0; v < N; ++v) {
+                    if (v == rank) continue;
                     int64_t lo, hi;
                     p.own_range(v, &lo, &hi);
-                    const uint16_t* src = v == rank ? shard + p.offset
-                                                    : static_cast<const uint16_t*>(rank_chunks[v]) + c[k];
-                    segs.push_back(CopySeg{src, dst + f[k] + lo, hi - lo, 0});
+                    segs.push_back(CopySeg{static_cast<const uint16_t*>(rank_chunks[v]) + c[k], dst + f[k] + lo, hi - lo,
+                                           nullptr, 0});
                 }
             }
             if ((s = build_copy_plan(L, std::move(key), segs, &plan)) != ZS3_OK) return s;
@@ -621,7 +667,7 @@ zs3_status zs3_gather_coalesced(zs3_layout_t L, int32_t rank, int32_t dtype, int
             uint16_t* dst = static_cast<uint16_t*>(own_chunk);
             for (int32_t k : order) {
                 const Slot& p = L->params[pos[k]];
-                segs.push_back(CopySeg{src + p.offset, dst + c[k], p.ps, 0});
+                segs.push_back(CopySeg{src + p.offset, dst + c[k], p.ps, nullptr, 0});
             }
             if ((s = build_copy_plan(L, std::move(key), segs, &plan)) != ZS3_OK) return s;
         }
@@ -641,7 +687,7 @@ zs3_status zs3_gather_coalesced(zs3_layout_t L, int32_t rank, int32_t dtype, int
                     int64_t lo, hi;
                     p.own_range(v, &lo, &hi);
                     const uint16_t* src = static_cast<const uint16_t*>(rank_chunks[v]) + c[k];
-                    segs.push_back(CopySeg{src, dst + f[k] + lo, hi - lo, 0});
+                    segs.push_back(CopySeg{src, dst + f[k] + lo, hi - lo, nullptr, 0});
                 }
             }
             if ((s = build_copy_plan(L, std::move(key), segs, &plan)) != ZS3_OK) return s;
@@ -708,18 +754,44 @@ zs3_status zs3_reduce_scatter_local(zs3_layout_t L, int32_t rank, int32_t dtype,
         Plan np;
         np.n_pieces = static_cast<int64_t>(pieces.size());
         np.co_aligned = co;
-        std::vector<size_t> offs;
-        s = upload(&np,
-                   {{segs.data(), segs.size() * sizeof(RsSeg)},
-                    {pieces.data(), pieces.size() * sizeof(Piece)},
-                    {srcs.data(), srcs.size() * sizeof(const uint16_t*)}},
-                   0, &offs);
-        if (s != ZS3_OK) return s;
-        np.off_segs = offs[0];
-        np.off_pieces = offs[1];
-        np.off_srcs = offs[2];
+        if (segs.size() <= static_cast<size_t>(kRsInlineSegs) &&
+            segs.size() * static_cast<size_t>(N) <= static_cast<size_t>(kRsInlineSrcs)) {
+            auto ri = std::make_shared<RsInline>();
+            std::memset(ri.get(), 0, sizeof(RsInline));
+            ri->nseg = static_cast<int32_t>(segs.size());
+            ri->world = N;
+            std::vector<int32_t> per_seg(segs.size(), 0);
+            for (const Piece& pc : pieces) ++per_seg[pc.seg];
+            int32_t npc = 0;
+            for (size_t i = 0; i < segs.size(); ++i) {
+                ri->piece_start[i] = npc;
+                npc += per_seg[i];
+                ri->head[i] = static_cast<int32_t>(((16u - (reinterpret_cast<uintptr_t>(segs[i].dst) & 15u)) & 15u) >> 1);
+                ri->dst[i] = segs[i].dst;
+                ri->real[i] = segs[i].real;
+                ri->total[i] = segs[i].total;
+                for (int32_t v = 0; v < N; ++v) ri->src[i * N + v] = srcs[segs[i].src_index + v];
+            }
+            ri->piece_start[segs.size()] = npc;
+            np.rs_inline = std::move(ri);
+        } else {
+            std::vector<size_t> offs;
+            s = upload(&np,
+                       {{segs.data(), segs.size() * sizeof(RsSeg)},
+                        {pieces.data(), pieces.size() * sizeof(Piece)},
+                        {srcs.data(), srcs.size() * sizeof(const uint16_t*)}},
+                       0, &offs);
+            if (s != ZS3_OK) return s;
+            np.off_segs = offs[0];
+            np.off_pieces = offs[1];
+            np.off_srcs = offs[2];
+        }
         store_plan(L, std::move(key), std::move(np), &plan);
     }
+    if (plan->rs_inline)
+        return hip_status(launch_reduce_scatter_inline(dtype, *plan->rs_inline, plan->co_aligned,
+                                                       static_cast<hipStream_t>(stream)),
+                          "reduce-scatter kernel launch");
     return hip_status(launch_reduce_scatter(dtype, plan->at<RsSeg>(plan->off_segs), plan->at<Piece>(plan->off_pieces),
                                             plan->n_pieces, plan->at<const uint16_t*>(plan->off_srcs), N,
                                             plan->co_aligned, static_cast<hipStream_t>(stream)),
@@ -842,12 +914,37 @@ zs3_status zs3_adam_step(zs3_layout_t L, int32_t rank, int32_t dtype, int64_t be
         if ((s = check_grid(static_cast<int64_t>(spans.size()), kAdamSub)) != ZS3_OK) return s;
         Plan np;
         np.n_pieces = static_cast<int64_t>(spans.size());
-        std::vector<size_t> offs;
-        s = upload(&np, {{spans.data(), spans.size() * sizeof(Span)}}, 0, &offs);
-        if (s != ZS3_OK) return s;
-        np.off_pieces = offs[0];
+        if (runs.size() <= static_cast<size_t>(kAdamInlineRuns)) {
+            auto ai = std::make_shared<AdamInline>();
+            std::memset(ai.get(), 0, sizeof(AdamInline));
+            ai->nrun = static_cast<int32_t>(runs.size());
+            int32_t np_ = 0;
+            size_t si = 0;
+            for (size_t i = 0; i < runs.size(); ++i) {
+                ai->piece_start[i] = np_;
+                ai->begin[i] = runs[i].first;
+                ai->count[i] = runs[i].second;
+                // spans of run i are consecutive in `spans`
+                while (si < spans.size() && spans[si].begin < runs[i].first + runs[i].second) {
+                    ++np_;
+                    ++si;
+                }
+            }
+            ai->piece_start[runs.size()] = np_;
+            np.adam_inline = std::move(ai);
+        } else {
+            std::vector<size_t> offs;
+            s = upload(&np, {{spans.data(), spans.size() * sizeof(Span)}}, 0, &offs);
+            if (s != ZS3_OK) return s;
+            np.off_pieces = offs[0];
+        }
         store_plan(L, std::move(key), std::move(np), &plan);
     }
+    if (plan->adam_inline)
+        return hip_status(launch_adam_inline(dtype, *plan->adam_inline, master, exp_avg, exp_avg_sq,
+                                             static_cast<const uint16_t*>(grad_flat), static_cast<uint16_t*>(shard_flat),
+                                             scale, nonfinite, c, vec_ok, static_cast<hipStream_t>(stream)),
+                          "Adam kernel launch");
     return hip_status(launch_adam(dtype, plan->at<Span>(plan->off_pieces), plan->n_pieces, master, exp_avg, exp_avg_sq,
                                   static_cast<const uint16_t*>(grad_flat), static_cast<uint16_t*>(shard_flat), scale,
                                   nonfinite, c, vec_ok, static_cast<hipStream_t>(stream)),

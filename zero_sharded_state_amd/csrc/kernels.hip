@@ -16,6 +16,7 @@
 // below is the sequence of IEEE operations it spells, with no fused
 // multiply-add.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "zs3_internal.hpp"
@@ -148,7 +149,8 @@ __device__ __forceinline__ v4u load_any(const uint16_t* p, uint32_t so) {
 // [sub*B*V, (sub+1)*B*V) and the last one the tail elements.
 
 template <int SO>
-__device__ __forceinline__ void copy_body(const uint16_t* src, uint16_t* dst, int64_t i0, int64_t nv, int t) {
+__device__ __forceinline__ void copy_body(const uint16_t* src, uint16_t* dst, uint16_t* dst2, int64_t n2,
+                                          int64_t i0, int64_t nv, int t) {
     v4u r[kCopyVPT];
 #pragma unroll
     for (int u = 0; u < kCopyVPT; ++u) {
@@ -158,29 +160,42 @@ __device__ __forceinline__ void copy_body(const uint16_t* src, uint16_t* dst, in
 #pragma unroll
     for (int u = 0; u < kCopyVPT; ++u) {
         const int64_t i = i0 + t + int64_t(u) * kBlock;
-        if (i < nv) st_stream<kNtCopy>(dst + 8 * i, r[u]);
+        if (i < nv) {
+            st_stream<kNtCopy>(dst + 8 * i, r[u]);
+            if (dst2 != nullptr && 8 * i < n2) {
+                if (8 * i + 8 <= n2) {
+                    st_stream<kNtCopy>(dst2 + 8 * i, r[u]);
+                } else {
+                    for (int e = 0; e < 8 && 8 * i + e < n2; ++e)
+                        dst2[8 * i + e] = static_cast<uint16_t>((e & 1) ? hi16(r[u][e >> 1]) : lo16(r[u][e >> 1]));
+                }
+            }
+        }
     }
 }
 
-// One body, four kernel names (partition, pack, unpack, fused gather) so
-// that profiles attribute time to each step of the method.
-template <int OP>
-__global__ __launch_bounds__(kBlock) void k_copy(const CopySeg* __restrict__ segs,
-                                                 const Piece* __restrict__ pieces) {
-    const uint32_t pidx = blockIdx.x / kCopySub;
-    const int sub = static_cast<int>(blockIdx.x % kCopySub);
-    const Piece pc = pieces[pidx];
-    const CopySeg sg = segs[pc.seg];
-    const int t = threadIdx.x;
-    uint16_t* dst = sg.dst + pc.begin;
-    const uint16_t* src = sg.src != nullptr ? sg.src + pc.begin : nullptr;
-    int64_t n = pc.len;
+// The work of one piece: elements [begin, begin + len) of a segment (and,
+// for a two-destination segment, of its second destination where the
+// segment's first count2 elements go).
+__device__ __forceinline__ void copy_piece(const uint16_t* seg_src, uint16_t* seg_dst, uint16_t* seg_dst2,
+                                           int64_t count2, int64_t begin, int64_t len, int sub, int t) {
+    uint16_t* dst = seg_dst + begin;
+    uint16_t* dst2 = seg_dst2 != nullptr ? seg_dst2 + begin : nullptr;
+    int64_t n2 = seg_dst2 != nullptr ? count2 - begin : 0;     // elements of this piece that also go to dst2
+    const uint16_t* src = seg_src != nullptr ? seg_src + begin : nullptr;
+    int64_t n = len;
     int64_t h = head16(dst);
     if (h > n) h = n;
-    if (sub == 0 && t < h) dst[t] = src != nullptr ? src[t] : uint16_t(0);
+    if (sub == 0 && t < h) {
+        const uint16_t x = src != nullptr ? src[t] : uint16_t(0);
+        dst[t] = x;
+        if (t < n2) dst2[t] = x;
+    }
     dst += h;
     n -= h;
     if (src != nullptr) src += h;
+    if (dst2 != nullptr) dst2 += h;
+    n2 -= h;
     const int64_t nv = n >> 3;
     const int64_t i0 = int64_t(sub) * kBlock * kCopyVPT;
     if (src == nullptr) {
@@ -192,18 +207,72 @@ __global__ __launch_bounds__(kBlock) void k_copy(const CopySeg* __restrict__ seg
         }
     } else {
         switch (static_cast<uint32_t>(reinterpret_cast<uintptr_t>(src)) & 15u) {
-            case 0: copy_body<0>(src, dst, i0, nv, t); break;
-            case 2: copy_body<2>(src, dst, i0, nv, t); break;
-            case 4: copy_body<4>(src, dst, i0, nv, t); break;
-            case 6: copy_body<6>(src, dst, i0, nv, t); break;
-            case 8: copy_body<8>(src, dst, i0, nv, t); break;
-            case 10: copy_body<10>(src, dst, i0, nv, t); break;
-            case 12: copy_body<12>(src, dst, i0, nv, t); break;
-            default: copy_body<14>(src, dst, i0, nv, t); break;
+            case 0: copy_body<0>(src, dst, dst2, n2, i0, nv, t); break;
+            case 2: copy_body<2>(src, dst, dst2, n2, i0, nv, t); break;
+            case 4: copy_body<4>(src, dst, dst2, n2, i0, nv, t); break;
+            case 6: copy_body<6>(src, dst, dst2, n2, i0, nv, t); break;
+            case 8: copy_body<8>(src, dst, dst2, n2, i0, nv, t); break;
+            case 10: copy_body<10>(src, dst, dst2, n2, i0, nv, t); break;
+            case 12: copy_body<12>(src, dst, dst2, n2, i0, nv, t); break;
+            default: copy_body<14>(src, dst, dst2, n2, i0, nv, t); break;
         }
     }
     const int64_t rem = n & 7;
-    if (sub == kCopySub - 1 && t < rem) dst[nv * 8 + t] = src != nullptr ? src[nv * 8 + t] : uint16_t(0);
+    if (sub == kCopySub - 1 && t < rem) {
+        const uint16_t x = src != nullptr ? src[nv * 8 + t] : uint16_t(0);
+        dst[nv * 8 + t] = x;
+        if (nv * 8 + t < n2) dst2[nv * 8 + t] = x;
+    }
+}
+
+// Piece `q` of a segment of `count` elements whose destination needs `head`
+// elements to reach 16-byte alignment: the same split as the host's work
+// lists (first piece head + P elements, then P at a time).
+__device__ __forceinline__ void piece_range(int64_t q, int64_t count, int64_t head, int64_t P, int64_t* begin,
+                                            int64_t* len) {
+    const int64_t first = count < head + P ? count : head + P;
+    if (q == 0) {
+        *begin = 0;
+        *len = first;
+    } else {
+        const int64_t b = first + (q - 1) * P;
+        *begin = b;
+        *len = count - b < P ? count - b : P;
+    }
+}
+
+// Segment holding piece `pidx`: the number of segment starts at or below it.
+template <int MAXSEG>
+__device__ __forceinline__ int find_seg(const int32_t (&piece_start)[MAXSEG + 1], int nseg, int32_t pidx) {
+    int s = 0;
+#pragma unroll
+    for (int j = 1; j < MAXSEG; ++j) s += (j < nseg && piece_start[j] <= pidx) ? 1 : 0;
+    return s;
+}
+
+// One body, four kernel names (partition, pack, unpack, fused gather) so
+// that profiles attribute time to each step of the method.  Two ways to
+// find the work: a device work list (k_copy) or, for calls with few
+// segments, the whole plan in the kernel arguments (k_copy_inline), which
+// saves the dependent loads of the list at the start of every launch.
+template <int OP>
+__global__ __launch_bounds__(kBlock) void k_copy(const CopySeg* __restrict__ segs,
+                                                 const Piece* __restrict__ pieces) {
+    const uint32_t pidx = blockIdx.x / kCopySub;
+    const int sub = static_cast<int>(blockIdx.x % kCopySub);
+    const Piece pc = pieces[pidx];
+    const CopySeg sg = segs[pc.seg];
+    copy_piece(sg.src, sg.dst, sg.dst2, sg.count2, pc.begin, pc.len, sub, threadIdx.x);
+}
+
+template <int OP>
+__global__ __launch_bounds__(kBlock) void k_copy_inline(const CopyInline plan) {
+    const int32_t pidx = static_cast<int32_t>(blockIdx.x / kCopySub);
+    const int sub = static_cast<int>(blockIdx.x % kCopySub);
+    const int s = find_seg<kCopyInlineSegs>(plan.piece_start, plan.nseg, pidx);
+    int64_t begin, len;
+    piece_range(pidx - plan.piece_start[s], plan.count[s], plan.head[s], kCopyPiece, &begin, &len);
+    copy_piece(plan.src[s], plan.dst[s], plan.dst2[s], plan.count2[s], begin, len, sub, threadIdx.x);
 }
 
 // ---------------------------------------------------- reduce-scatter kernel
@@ -222,37 +291,40 @@ struct Divider {
     }
 };
 
-template <int D>
-__device__ __forceinline__ uint16_t rs_elem(const uint16_t* const* sp, int world, Divider div,
-                                            int64_t k, int64_t real) {
+// Source pointers of one segment: from a device table or from the kernel
+// arguments.
+struct TableSrcs {
+    const uint16_t* const* p;
+    __device__ __forceinline__ const uint16_t* operator()(int v) const { return p[v]; }
+};
+struct InlineSrcs {
+    const RsInline& plan;
+    int base;
+    __device__ __forceinline__ const uint16_t* operator()(int v) const { return plan.src[base + v]; }
+};
+
+template <int D, class SRC>
+__device__ __forceinline__ uint16_t rs_elem(const SRC& sp, int world, Divider div, int64_t k, int64_t real) {
     if (k >= real) return 0;
     float acc = 0.0f;
-    for (int v = 0; v < world; ++v) acc += widen<D>(sp[v][k]);
+    for (int v = 0; v < world; ++v) acc += widen<D>(sp(v)[k]);
     return static_cast<uint16_t>(narrow<D>(div(acc)));
 }
 
-template <int D, bool ALIGNED>
-__global__ __launch_bounds__(kBlock) void k_reduce_scatter(const RsSeg* __restrict__ segs,
-                                                           const Piece* __restrict__ pieces,
-                                                           const uint16_t* const* __restrict__ srcs,
-                                                           int world, Divider div) {
-    const uint32_t pidx = blockIdx.x / kRsSub;
-    const int sub = static_cast<int>(blockIdx.x % kRsSub);
-    const Piece pc = pieces[pidx];
-    const RsSeg sg = segs[pc.seg];
-    const int t = threadIdx.x;
-    const uint16_t* const* sp = srcs + sg.src_index;
-    int64_t k0 = pc.begin;
-    int64_t n = pc.len;
-    uint16_t* dst = sg.dst + k0;
+template <int D, bool ALIGNED, class SRC>
+__device__ __forceinline__ void rs_piece(const SRC& sp, uint16_t* seg_dst, int64_t real, int64_t begin,
+                                         int64_t len, int world, Divider div, int sub, int t) {
+    int64_t k0 = begin;
+    int64_t n = len;
+    uint16_t* dst = seg_dst + k0;
     int64_t h = head16(dst);
     if (h > n) h = n;
-    if (sub == 0 && t < h) dst[t] = rs_elem<D>(sp, world, div, k0 + t, sg.real);
+    if (sub == 0 && t < h) dst[t] = rs_elem<D>(sp, world, div, k0 + t, real);
     k0 += h;
     dst += h;
     n -= h;
     const int64_t nv = n >> 3;
-    int64_t nfull = sg.real > k0 ? (sg.real - k0) >> 3 : 0;
+    int64_t nfull = real > k0 ? (real - k0) >> 3 : 0;
     if (nfull > nv) nfull = nv;
     const int64_t i0 = int64_t(sub) * kBlock * kRsVPT;
 
@@ -262,33 +334,44 @@ __global__ __launch_bounds__(kBlock) void k_reduce_scatter(const RsSeg* __restri
         for (int u = 0; u < kRsVPT; ++u)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
-#pragma unroll 4
-        for (int v = 0; v < world; ++v) {
-            const uint16_t* s = sp[v] + k0;
-            v4u x[kRsVPT];
-            if constexpr (ALIGNED) {
+        // Sources in batches of kRsBatch: all loads of a batch are issued
+        // before its adds, which then run in rank order.
+        for (int vb = 0; vb < world; vb += kRsBatch) {
+            v4u x[kRsBatch][kRsVPT];
 #pragma unroll
-                for (int u = 0; u < kRsVPT; ++u) {
-                    const int64_t i = i0 + t + int64_t(u) * kBlock;
-                    if (i < nfull) x[u] = ld_stream<kNtRs>(s + 8 * i);
-                }
-            } else {
-                const uint32_t so = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s)) & 15u;
+            for (int j = 0; j < kRsBatch; ++j) {
+                if (vb + j < world) {
+                    const uint16_t* s = sp(vb + j) + k0;
+                    if constexpr (ALIGNED) {
 #pragma unroll
-                for (int u = 0; u < kRsVPT; ++u) {
-                    const int64_t i = i0 + t + int64_t(u) * kBlock;
-                    if (i < nfull) x[u] = load_any<kNtRs>(s + 8 * i, so);
+                        for (int u = 0; u < kRsVPT; ++u) {
+                            const int64_t i = i0 + t + int64_t(u) * kBlock;
+                            if (i < nfull) x[j][u] = ld_stream<kNtRs>(s + 8 * i);
+                        }
+                    } else {
+                        const uint32_t so = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s)) & 15u;
+#pragma unroll
+                        for (int u = 0; u < kRsVPT; ++u) {
+                            const int64_t i = i0 + t + int64_t(u) * kBlock;
+                            if (i < nfull) x[j][u] = load_any<kNtRs>(s + 8 * i, so);
+                        }
+                    }
                 }
             }
 #pragma unroll
-            for (int u = 0; u < kRsVPT; ++u) {
-                const int64_t i = i0 + t + int64_t(u) * kBlock;
-                if (i < nfull) {
+            for (int j = 0; j < kRsBatch; ++j) {
+                if (vb + j < world) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint32_t w = x[u][q];
-                        acc[u][2 * q] += widen<D>(lo16(w));
-                        acc[u][2 * q + 1] += widen<D>(hi16(w));
+                    for (int u = 0; u < kRsVPT; ++u) {
+                        const int64_t i = i0 + t + int64_t(u) * kBlock;
+                        if (i < nfull) {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const uint32_t w = x[j][u][q];
+                                acc[u][2 * q] += widen<D>(lo16(w));
+                                acc[u][2 * q + 1] += widen<D>(hi16(w));
+                            }
+                        }
                     }
                 }
             }
@@ -311,10 +394,34 @@ __global__ __launch_bounds__(kBlock) void k_reduce_scatter(const RsSeg* __restri
     int64_t hi = i0 + int64_t(kBlock) * kRsVPT;
     if (hi > nv) hi = nv;
     for (int64_t i = lo + t; i < hi; i += kBlock) {
-        for (int e = 0; e < 8; ++e) dst[8 * i + e] = rs_elem<D>(sp, world, div, k0 + 8 * i + e, sg.real);
+        for (int e = 0; e < 8; ++e) dst[8 * i + e] = rs_elem<D>(sp, world, div, k0 + 8 * i + e, real);
     }
     const int64_t rem = n & 7;
-    if (sub == kRsSub - 1 && t < rem) dst[nv * 8 + t] = rs_elem<D>(sp, world, div, k0 + nv * 8 + t, sg.real);
+    if (sub == kRsSub - 1 && t < rem) dst[nv * 8 + t] = rs_elem<D>(sp, world, div, k0 + nv * 8 + t, real);
+}
+
+template <int D, bool ALIGNED>
+__global__ __launch_bounds__(kBlock) void k_reduce_scatter(const RsSeg* __restrict__ segs,
+                                                           const Piece* __restrict__ pieces,
+                                                           const uint16_t* const* __restrict__ srcs,
+                                                           int world, Divider div) {
+    const uint32_t pidx = blockIdx.x / kRsSub;
+    const int sub = static_cast<int>(blockIdx.x % kRsSub);
+    const Piece pc = pieces[pidx];
+    const RsSeg sg = segs[pc.seg];
+    const TableSrcs sp{srcs + sg.src_index};
+    rs_piece<D, ALIGNED>(sp, sg.dst, sg.real, pc.begin, pc.len, world, div, sub, threadIdx.x);
+}
+
+template <int D, bool ALIGNED>
+__global__ __launch_bounds__(kBlock) void k_reduce_scatter_inline(const RsInline plan, Divider div) {
+    const int32_t pidx = static_cast<int32_t>(blockIdx.x / kRsSub);
+    const int sub = static_cast<int>(blockIdx.x % kRsSub);
+    const int s = find_seg<kRsInlineSegs>(plan.piece_start, plan.nseg, pidx);
+    int64_t begin, len;
+    piece_range(pidx - plan.piece_start[s], plan.total[s], plan.head[s], kRsPiece, &begin, &len);
+    const InlineSrcs sp{plan, s * plan.world};
+    rs_piece<D, ALIGNED>(sp, plan.dst[s], plan.real[s], begin, len, plan.world, div, sub, threadIdx.x);
 }
 
 // ------------------------------------------------------------ grad norm
@@ -470,28 +577,22 @@ __device__ __forceinline__ void adam_scalar(int64_t e, float* w, float* m, float
     s[e] = static_cast<uint16_t>(narrow<D>(ww));
 }
 
+// Elements [b, b + n) of the flat arrays, one piece, sub-block `sub`.
+// `skip` (the non-finite flag) is tested only after the vector loads are
+// issued, so its load never delays them; a skipped step writes nothing.
 template <int D, bool VEC>
-__global__ __launch_bounds__(kBlock) void k_adam(const Span* __restrict__ spans, float* __restrict__ w,
-                                                 float* __restrict__ m, float* __restrict__ v,
-                                                 const uint16_t* __restrict__ g, uint16_t* __restrict__ s,
-                                                 const float* __restrict__ scale_p,
-                                                 const int32_t* __restrict__ nonfinite_p, AdamConsts c) {
-    if (nonfinite_p != nullptr && *nonfinite_p != 0) return;
-    const float scale = *scale_p;
-    const uint32_t pidx = blockIdx.x / kAdamSub;
-    const int sub = static_cast<int>(blockIdx.x % kAdamSub);
-    const Span sp = spans[pidx];
-    const int t = threadIdx.x;
-    int64_t b = sp.begin;
-    int64_t n = sp.len;
+__device__ __forceinline__ void adam_piece(int64_t b, int64_t n, int sub, int t, float* __restrict__ w,
+                                           float* __restrict__ m, float* __restrict__ v,
+                                           const uint16_t* __restrict__ g, uint16_t* __restrict__ s, float scale,
+                                           bool skip, const AdamConsts& c) {
     if constexpr (!VEC) {
+        if (skip) return;
         for (int64_t i = int64_t(sub) * kBlock + t; i < n; i += int64_t(kBlock) * kAdamSub)
             adam_scalar<D>(b + i, w, m, v, g, s, scale, c);
         return;
     } else {
         int64_t h = (8 - (b & 7)) & 7;     // with 16-byte aligned bases, index % 8 == 0 is aligned for all
         if (h > n) h = n;
-        if (sub == 0 && t < h) adam_scalar<D>(b + t, w, m, v, g, s, scale, c);
         b += h;
         n -= h;
         const int64_t ng = n >> 3;
@@ -503,15 +604,17 @@ __global__ __launch_bounds__(kBlock) void k_adam(const Span* __restrict__ spans,
             const int64_t i = i0 + t + int64_t(u) * kBlock;
             if (i < ng) {
                 const int64_t e = b + 8 * i;
-                W[u][0] = ld_stream_f<kNtAdam>(w + e);
-                W[u][1] = ld_stream_f<kNtAdam>(w + e + 4);
-                M[u][0] = ld_stream_f<kNtAdam>(m + e);
-                M[u][1] = ld_stream_f<kNtAdam>(m + e + 4);
-                V[u][0] = ld_stream_f<kNtAdam>(v + e);
-                V[u][1] = ld_stream_f<kNtAdam>(v + e + 4);
-                G[u] = ld_stream<kNtAdam>(g + e);
+                W[u][0] = ld_stream_f<kNtAdamLd>(w + e);
+                W[u][1] = ld_stream_f<kNtAdamLd>(w + e + 4);
+                M[u][0] = ld_stream_f<kNtAdamLd>(m + e);
+                M[u][1] = ld_stream_f<kNtAdamLd>(m + e + 4);
+                V[u][0] = ld_stream_f<kNtAdamLd>(v + e);
+                V[u][1] = ld_stream_f<kNtAdamLd>(v + e + 4);
+                G[u] = ld_stream<kNtAdamLd>(g + e);
             }
         }
+        if (skip) return;
+        if (sub == 0 && t < h) adam_scalar<D>(b - h + t, w, m, v, g, s, scale, c);
 #pragma unroll
         for (int u = 0; u < kAdamGPT; ++u) {
             const int64_t i = i0 + t + int64_t(u) * kBlock;
@@ -532,14 +635,14 @@ __global__ __launch_bounds__(kBlock) void k_adam(const Span* __restrict__ spans,
                     adam1(ww[q], mm[q], vv[q], gf, scale, c);
                     out[q] = narrow<D>(ww[q]);
                 }
-                st_stream_f<kNtAdam>(w + e, v4f{ww[0], ww[1], ww[2], ww[3]});
-                st_stream_f<kNtAdam>(w + e + 4, v4f{ww[4], ww[5], ww[6], ww[7]});
-                st_stream_f<kNtAdam>(m + e, v4f{mm[0], mm[1], mm[2], mm[3]});
-                st_stream_f<kNtAdam>(m + e + 4, v4f{mm[4], mm[5], mm[6], mm[7]});
-                st_stream_f<kNtAdam>(v + e, v4f{vv[0], vv[1], vv[2], vv[3]});
-                st_stream_f<kNtAdam>(v + e + 4, v4f{vv[4], vv[5], vv[6], vv[7]});
-                st_stream<kNtAdam>(s + e, v4u{pack2(out[0], out[1]), pack2(out[2], out[3]),
-                                     pack2(out[4], out[5]), pack2(out[6], out[7])});
+                st_stream_f<kNtAdamSt>(w + e, v4f{ww[0], ww[1], ww[2], ww[3]});
+                st_stream_f<kNtAdamSt>(w + e + 4, v4f{ww[4], ww[5], ww[6], ww[7]});
+                st_stream_f<kNtAdamSt>(m + e, v4f{mm[0], mm[1], mm[2], mm[3]});
+                st_stream_f<kNtAdamSt>(m + e + 4, v4f{mm[4], mm[5], mm[6], mm[7]});
+                st_stream_f<kNtAdamSt>(v + e, v4f{vv[0], vv[1], vv[2], vv[3]});
+                st_stream_f<kNtAdamSt>(v + e + 4, v4f{vv[4], vv[5], vv[6], vv[7]});
+                st_stream<kNtAdamSt>(s + e, v4u{pack2(out[0], out[1]), pack2(out[2], out[3]),
+                                              pack2(out[4], out[5]), pack2(out[6], out[7])});
             }
         }
         const int64_t rem = n & 7;
@@ -547,9 +650,64 @@ __global__ __launch_bounds__(kBlock) void k_adam(const Span* __restrict__ spans,
     }
 }
 
+// The skip flag, the scale and the work description are read before any of
+// them is tested, so their loads overlap instead of queueing one behind the
+// other at the start of every (short-lived) workgroup.
+template <int D, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_adam(const Span* __restrict__ spans, float* __restrict__ w,
+                                                 float* __restrict__ m, float* __restrict__ v,
+                                                 const uint16_t* __restrict__ g, uint16_t* __restrict__ s,
+                                                 const float* __restrict__ scale_p,
+                                                 const int32_t* __restrict__ nonfinite_p, AdamConsts c) {
+    const uint32_t pidx = blockIdx.x / kAdamSub;
+    const int sub = static_cast<int>(blockIdx.x % kAdamSub);
+    const int32_t flag = nonfinite_p != nullptr ? *nonfinite_p : 0;
+    const float scale = *scale_p;
+    const Span sp = spans[pidx];
+    adam_piece<D, VEC>(sp.begin, sp.len, sub, threadIdx.x, w, m, v, g, s, scale, flag != 0, c);
+}
+
+template <int D, bool VEC>
+__global__ __launch_bounds__(kBlock) void k_adam_inline(const AdamInline plan, float* __restrict__ w,
+                                                        float* __restrict__ m, float* __restrict__ v,
+                                                        const uint16_t* __restrict__ g, uint16_t* __restrict__ s,
+                                                        const float* __restrict__ scale_p,
+                                                        const int32_t* __restrict__ nonfinite_p, AdamConsts c) {
+    const int32_t pidx = static_cast<int32_t>(blockIdx.x / kAdamSub);
+    const int sub = static_cast<int>(blockIdx.x % kAdamSub);
+    const int32_t flag = nonfinite_p != nullptr ? *nonfinite_p : 0;
+    const float scale = *scale_p;
+    const int r = find_seg<kAdamInlineRuns>(plan.piece_start, plan.nrun, pidx);
+    int64_t begin, len;
+    const int64_t b0 = plan.begin[r];
+    piece_range(pidx - plan.piece_start[r], plan.count[r], (8 - (b0 & 7)) & 7, kAdamPiece, &begin, &len);
+    adam_piece<D, VEC>(b0 + begin, len, sub, threadIdx.x, w, m, v, g, s, scale, flag != 0, c);
+}
+
 inline dim3 grid_of(int64_t n) { return dim3(static_cast<uint32_t>(n)); }
 
+// Timing hook: when a host thread has set events, its next launch records
+// the kernel's own start and end timestamps into them (hipExtLaunchKernel).
+thread_local hipEvent_t t_start = nullptr;
+thread_local hipEvent_t t_stop = nullptr;
+
+template <typename K, typename... A>
+void launch(K kernel, dim3 grid, dim3 block, hipStream_t stream, A... args) {
+    if (t_start != nullptr || t_stop != nullptr) {
+        hipEvent_t a = t_start, b = t_stop;
+        t_start = t_stop = nullptr;
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, a, b, 0, args...);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+    }
+}
+
 }  // namespace
+
+void set_launch_events(hipEvent_t start, hipEvent_t stop) {
+    t_start = start;
+    t_stop = stop;
+}
 
 // ---------------------------------------------------------------- launchers
 
@@ -558,29 +716,62 @@ hipError_t launch_copy(CopyKind kind, const CopySeg* segs, const Piece* pieces, 
     if (n_pieces <= 0) return hipSuccess;
     const dim3 g = grid_of(n_pieces * kCopySub), b(kBlock);
     switch (kind) {
-        case kCopyPartition: hipLaunchKernelGGL(k_copy<kCopyPartition>, g, b, 0, stream, segs, pieces); break;
-        case kCopyPack: hipLaunchKernelGGL(k_copy<kCopyPack>, g, b, 0, stream, segs, pieces); break;
-        case kCopyUnpack: hipLaunchKernelGGL(k_copy<kCopyUnpack>, g, b, 0, stream, segs, pieces); break;
-        default: hipLaunchKernelGGL(k_copy<kCopyGather>, g, b, 0, stream, segs, pieces); break;
+        case kCopyPartition: launch(k_copy<kCopyPartition>, g, b, stream, segs, pieces); break;
+        case kCopyPack: launch(k_copy<kCopyPack>, g, b, stream, segs, pieces); break;
+        case kCopyUnpack: launch(k_copy<kCopyUnpack>, g, b, stream, segs, pieces); break;
+        default: launch(k_copy<kCopyGather>, g, b, stream, segs, pieces); break;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_copy_inline(CopyKind kind, const CopyInline& plan, hipStream_t stream) {
+    const int64_t n_pieces = plan.piece_start[plan.nseg];
+    if (n_pieces <= 0) return hipSuccess;
+    const dim3 g = grid_of(n_pieces * kCopySub), b(kBlock);
+    switch (kind) {
+        case kCopyPartition: launch(k_copy_inline<kCopyPartition>, g, b, stream, plan); break;
+        case kCopyPack: launch(k_copy_inline<kCopyPack>, g, b, stream, plan); break;
+        case kCopyUnpack: launch(k_copy_inline<kCopyUnpack>, g, b, stream, plan); break;
+        default: launch(k_copy_inline<kCopyGather>, g, b, stream, plan); break;
+    }
+    return hipGetLastError();
+}
+
+static Divider make_divider(int32_t world) {
+    Divider div;
+    div.n = static_cast<float>(world);
+    div.pow2 = (world & (world - 1)) == 0;
+    div.inv = 1.0f / static_cast<float>(world);
+    return div;
 }
 
 hipError_t launch_reduce_scatter(int32_t dtype, const RsSeg* segs, const Piece* pieces, int64_t n_pieces,
                                  const uint16_t* const* srcs, int32_t world, bool co_aligned,
                                  hipStream_t stream) {
     if (n_pieces <= 0) return hipSuccess;
-    Divider div;
-    div.n = static_cast<float>(world);
-    div.pow2 = (world & (world - 1)) == 0;
-    div.inv = 1.0f / static_cast<float>(world);
+    const Divider div = make_divider(world);
     const dim3 g = grid_of(n_pieces * kRsSub), b(kBlock);
     if (dtype == kFP16) {
-        if (co_aligned) hipLaunchKernelGGL((k_reduce_scatter<kFP16, true>), g, b, 0, stream, segs, pieces, srcs, world, div);
-        else hipLaunchKernelGGL((k_reduce_scatter<kFP16, false>), g, b, 0, stream, segs, pieces, srcs, world, div);
+        if (co_aligned) launch((k_reduce_scatter<kFP16, true>), g, b, stream, segs, pieces, srcs, world, div);
+        else launch((k_reduce_scatter<kFP16, false>), g, b, stream, segs, pieces, srcs, world, div);
     } else {
-        if (co_aligned) hipLaunchKernelGGL((k_reduce_scatter<kBF16, true>), g, b, 0, stream, segs, pieces, srcs, world, div);
-        else hipLaunchKernelGGL((k_reduce_scatter<kBF16, false>), g, b, 0, stream, segs, pieces, srcs, world, div);
+        if (co_aligned) launch((k_reduce_scatter<kBF16, true>), g, b, stream, segs, pieces, srcs, world, div);
+        else launch((k_reduce_scatter<kBF16, false>), g, b, stream, segs, pieces, srcs, world, div);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_scatter_inline(int32_t dtype, const RsInline& plan, bool co_aligned, hipStream_t stream) {
+    const int64_t n_pieces = plan.piece_start[plan.nseg];
+    if (n_pieces <= 0) return hipSuccess;
+    const Divider div = make_divider(plan.world);
+    const dim3 g = grid_of(n_pieces * kRsSub), b(kBlock);
+    if (dtype == kFP16) {
+        if (co_aligned) launch((k_reduce_scatter_inline<kFP16, true>), g, b, stream, plan, div);
+        else launch((k_reduce_scatter_inline<kFP16, false>), g, b, stream, plan, div);
+    } else {
+        if (co_aligned) launch((k_reduce_scatter_inline<kBF16, true>), g, b, stream, plan, div);
+        else launch((k_reduce_scatter_inline<kBF16, false>), g, b, stream, plan, div);
     }
     return hipGetLastError();
 }
@@ -591,13 +782,13 @@ hipError_t launch_grad_norm(int32_t dtype, const uint16_t* grad, const Span* spa
                             float* scale_out, int32_t* nonfinite, hipStream_t stream) {
     if (n_blocks > 0) {
         if (dtype == kFP16)
-            hipLaunchKernelGGL(k_sumsq<kFP16>, grid_of(n_blocks), dim3(kBlock), 0, stream, grad, spans, n_spans, n_part, partials);
+            launch(k_sumsq<kFP16>, grid_of(n_blocks), dim3(kBlock), stream, grad, spans, n_spans, n_part, partials);
         else
-            hipLaunchKernelGGL(k_sumsq<kBF16>, grid_of(n_blocks), dim3(kBlock), 0, stream, grad, spans, n_spans, n_part, partials);
+            launch(k_sumsq<kBF16>, grid_of(n_blocks), dim3(kBlock), stream, grad, spans, n_spans, n_part, partials);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_norm_finalize, dim3(1), dim3(kBlock), 0, stream, partials, n_blocks, sumsq, rank, world,
+    launch(k_norm_finalize, dim3(1), dim3(kBlock), stream, partials, n_blocks, sumsq, rank, world,
                        finalize, max_norm, loss_scale, norm_out, scale_out, nonfinite);
     return hipGetLastError();
 }
@@ -608,11 +799,27 @@ hipError_t launch_adam(int32_t dtype, const Span* spans, int64_t n_spans, float*
     if (n_spans <= 0) return hipSuccess;
     const dim3 g = grid_of(n_spans * kAdamSub), b(kBlock);
     if (dtype == kFP16) {
-        if (vec_ok) hipLaunchKernelGGL((k_adam<kFP16, true>), g, b, 0, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
-        else hipLaunchKernelGGL((k_adam<kFP16, false>), g, b, 0, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
+        if (vec_ok) launch((k_adam<kFP16, true>), g, b, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
+        else launch((k_adam<kFP16, false>), g, b, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
     } else {
-        if (vec_ok) hipLaunchKernelGGL((k_adam<kBF16, true>), g, b, 0, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
-        else hipLaunchKernelGGL((k_adam<kBF16, false>), g, b, 0, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
+        if (vec_ok) launch((k_adam<kBF16, true>), g, b, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
+        else launch((k_adam<kBF16, false>), g, b, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_adam_inline(int32_t dtype, const AdamInline& plan, float* master, float* exp_avg,
+                              float* exp_avg_sq, const uint16_t* grad, uint16_t* shard, const float* scale,
+                              const int32_t* nonfinite, const AdamConsts& c, bool vec_ok, hipStream_t stream) {
+    const int64_t n_pieces = plan.piece_start[plan.nrun];
+    if (n_pieces <= 0) return hipSuccess;
+    const dim3 g = grid_of(n_pieces * kAdamSub), b(kBlock);
+    if (dtype == kFP16) {
+        if (vec_ok) launch((k_adam_inline<kFP16, true>), g, b, stream, plan, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
+        else launch((k_adam_inline<kFP16, false>), g, b, stream, plan, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
+    } else {
+        if (vec_ok) launch((k_adam_inline<kBF16, true>), g, b, stream, plan, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
+        else launch((k_adam_inline<kBF16, false>), g, b, stream, plan, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
     }
     return hipGetLastError();
 }

@@ -28,6 +28,9 @@ constexpr int kBlock = 256;             // threads per workgroup (4 wave64)
 #ifndef ZS3_RS_SUB
 #define ZS3_RS_SUB 8
 #endif
+#ifndef ZS3_RS_BATCH
+#define ZS3_RS_BATCH 8
+#endif
 #ifndef ZS3_NORM_VPT
 #define ZS3_NORM_VPT 2
 #endif
@@ -61,6 +64,7 @@ constexpr int64_t kCopyPiece = int64_t(kBlock) * kCopyVPT * 8 * kCopySub;
 constexpr int kRsVPT = ZS3_RS_VPT;
 constexpr int kRsSub = ZS3_RS_SUB;
 constexpr int64_t kRsPiece = int64_t(kBlock) * kRsVPT * 8 * kRsSub;
+constexpr int kRsBatch = ZS3_RS_BATCH;     // sources whose loads are issued together
 constexpr int kNormVPT = ZS3_NORM_VPT;     // vectors per thread per loop trip
 constexpr int kNormGrid = ZS3_NORM_GRID;   // workgroups of the sum-of-squares pass (upper bound)
 constexpr int kNormSub = 8;
@@ -71,14 +75,18 @@ constexpr int64_t kAdamPiece = int64_t(kBlock) * kAdamGPT * 8 * kAdamSub;
 constexpr bool kNtCopy = ZS3_NT_COPY != 0;
 constexpr bool kNtRs = ZS3_NT_RS != 0;
 constexpr bool kNtNorm = ZS3_NT_NORM != 0;
-constexpr bool kNtAdam = ZS3_NT_ADAM != 0;
+constexpr bool kNtAdamLd = ZS3_NT_ADAM == 1 || ZS3_NT_ADAM == 2;   // 1: loads and stores, 2: loads only
+constexpr bool kNtAdamSt = ZS3_NT_ADAM == 1 || ZS3_NT_ADAM == 3;   // 3: stores only
 
-// A contiguous copy: dst[0 .. count) = src[0 .. count), or zeros if src is null.
+// A contiguous copy: dst[0 .. count) = src[0 .. count), or zeros if src is
+// null; if dst2 is set, also dst2[0 .. count2) = src[0 .. count2) from the
+// same loads (count2 <= count, dst2 at the same address mod 16 as dst).
 struct CopySeg {
     const uint16_t* src;
     uint16_t* dst;
     int64_t count;
-    int64_t reserved;
+    uint16_t* dst2;
+    int64_t count2;
 };
 
 // One workgroup's share of a segment: elements [begin, begin + len) of it.
@@ -95,6 +103,44 @@ struct RsSeg {
     int64_t real;        // averaged elements
     int64_t total;       // real + padding zeros (the partition size)
     int64_t src_index;
+};
+
+// Calls with few segments carry their whole plan in the kernel arguments
+// (structure of arrays, < 2 KB each): the workgroup finds its segment from
+// the prefix of piece counts and computes its range, with no loads before
+// the data.  piece_start[nseg] is the total number of pieces.
+constexpr int kCopyInlineSegs = 40;
+struct CopyInline {
+    int32_t nseg;
+    int32_t piece_start[kCopyInlineSegs + 1];
+    int32_t head[kCopyInlineSegs];            // elements before the destination is 16-byte aligned
+    const uint16_t* src[kCopyInlineSegs];     // null: fill with zeros
+    uint16_t* dst[kCopyInlineSegs];
+    int64_t count[kCopyInlineSegs];
+    uint16_t* dst2[kCopyInlineSegs];          // optional second destination (see CopySeg)
+    int64_t count2[kCopyInlineSegs];
+};
+
+constexpr int kRsInlineSegs = 8;
+constexpr int kRsInlineSrcs = 128;
+struct RsInline {
+    int32_t nseg;
+    int32_t world;
+    int32_t piece_start[kRsInlineSegs + 1];
+    int32_t head[kRsInlineSegs];
+    uint16_t* dst[kRsInlineSegs];
+    int64_t real[kRsInlineSegs];
+    int64_t total[kRsInlineSegs];
+    const uint16_t* src[kRsInlineSrcs];       // segment s, rank v at [s * world + v]
+};
+
+// Adam over a few long runs of real elements: the runs in the kernel arguments.
+constexpr int kAdamInlineRuns = 16;
+struct AdamInline {
+    int32_t nrun;
+    int32_t piece_start[kAdamInlineRuns + 1];
+    int64_t begin[kAdamInlineRuns];
+    int64_t count[kAdamInlineRuns];
 };
 
 // A run of flat-array positions handled by one workgroup (norm, Adam):
@@ -118,8 +164,15 @@ enum DType : int32_t { kFP16 = 1, kBF16 = 2 };
 enum CopyKind : int32_t { kCopyPartition = 1, kCopyPack = 2, kCopyUnpack = 3, kCopyGather = 4 };
 
 // ---- launchers (kernels.hip) -------------------------------------------
+// The calling thread's next launch records its start/end into these events.
+void set_launch_events(hipEvent_t start, hipEvent_t stop);
+
 hipError_t launch_copy(CopyKind kind, const CopySeg* segs, const Piece* pieces, int64_t n_pieces,
                        hipStream_t stream);
+
+hipError_t launch_copy_inline(CopyKind kind, const CopyInline& plan, hipStream_t stream);
+hipError_t launch_reduce_scatter_inline(int32_t dtype, const RsInline& plan, bool co_aligned,
+                                        hipStream_t stream);
 
 hipError_t launch_reduce_scatter(int32_t dtype, const RsSeg* segs, const Piece* pieces,
                                  int64_t n_pieces, const uint16_t* const* srcs, int32_t world,
@@ -133,6 +186,10 @@ hipError_t launch_grad_norm(int32_t dtype, const uint16_t* grad, const Span* spa
                             int64_t n_part, int64_t n_blocks, double* partials, double* sumsq, int32_t rank,
                             int32_t world, int32_t finalize, double max_norm, double loss_scale, double* norm_out,
                             float* scale_out, int32_t* nonfinite, hipStream_t stream);
+
+hipError_t launch_adam_inline(int32_t dtype, const AdamInline& plan, float* master, float* exp_avg,
+                              float* exp_avg_sq, const uint16_t* grad, uint16_t* shard, const float* scale,
+                              const int32_t* nonfinite, const AdamConsts& c, bool vec_ok, hipStream_t stream);
 
 hipError_t launch_adam(int32_t dtype, const Span* spans, int64_t n_spans, float* master,
                        float* exp_avg, float* exp_avg_sq, const uint16_t* grad, uint16_t* shard,

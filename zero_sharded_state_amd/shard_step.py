@@ -46,7 +46,7 @@ class ShardStep:
     def __init__(self, *, world_size: int, rank: int, threshold: int, ds_ids: Sequence[int],
                  numels: Sequence[int], dtype: str, prefetch_bucket_size: int, reduce_bucket_size: int,
                  sub_group_size: int, adam: AdamConfig = AdamConfig(), max_norm: float = 1.0,
-                 device: str = "cuda", rs_streams: int = 4):
+                 device: str = "cuda", rs_streams: int = 1, gather_streams: int = 1):
         import torch
 
         self.torch = torch
@@ -96,15 +96,22 @@ class ShardStep:
         self.shard = torch.zeros(max(1, self.S), dtype=i16, device=dev)
         self.grad = torch.zeros(max(1, self.S), dtype=i16, device=dev)
         self.recv = torch.zeros(max(1, self.N * self.S), dtype=i16, device=dev)  # slices sent to this rank
-        self.master = torch.zeros(max(1, self.S), dtype=f32, device=dev)
-        self.exp_avg = torch.zeros_like(self.master)
-        self.exp_avg_sq = torch.zeros_like(self.master)
+        # the fp32 optimizer partition (master, momentum, variance) is one
+        # allocation, each array starting on a 2 MiB boundary
+        sa = (max(1, self.S) + (1 << 19) - 1) >> 19 << 19
+        self.state = torch.zeros(3 * sa, dtype=f32, device=dev)
+        self.master = self.state[0:max(1, self.S)]
+        self.exp_avg = self.state[sa:sa + max(1, self.S)]
+        self.exp_avg_sq = self.state[2 * sa:2 * sa + max(1, self.S)]
         self.sumsq = torch.zeros(self.N + 1, dtype=torch.float64, device=dev)
         self.outs = torch.zeros(2, dtype=torch.float64, device=dev)   # norm | scale (f32), flag (i32)
         self.t = 0
         # independent gradient buckets are spread over a few streams so that
         # short reduce-scatter kernels overlap (default priority streams)
-        self.aux_streams = [torch.cuda.Stream(device=dev) for _ in range(max(0, rs_streams - 1))]
+        n_aux = max(0, max(rs_streams, gather_streams) - 1)
+        self.aux_streams = [torch.cuda.Stream(device=dev) for _ in range(n_aux)]
+        self.rs_streams = max(1, rs_streams)
+        self.gather_streams = max(1, gather_streams)
         self._fork = torch.cuda.Event()
         self._joins = [torch.cuda.Event() for _ in self.aux_streams]
         self._marshal()
@@ -183,29 +190,44 @@ class ShardStep:
                                                chunks, fullp, None,
                                                stream if stream is not None else self._stream()))
 
-    def gather_pass(self, stream=None):
-        s = stream if stream is not None else self._stream()
+    def _fanout(self, stream, k):
+        """The main stream plus k-1 auxiliary streams that wait for it."""
+        torch = self.torch
+        main = torch.cuda.current_stream() if stream is None else stream
+        aux = self.aux_streams[:k - 1]
+        if aux:
+            self._fork.record(main)
+            for a in aux:
+                a.wait_event(self._fork)
+        return main, aux, [int(main.cuda_stream)] + [int(a.cuda_stream) for a in aux]
+
+    def _join(self, main, aux):
+        for a, e in zip(aux, self._joins):
+            e.record(a)
+            main.wait_event(e)
+
+    def gather_pass(self, stream=None, timer=None):
+        """Every gather bucket; buckets are independent, so with several
+        gather streams they are dealt round-robin and joined at the end.
+        ``timer()``, if given, returns a (start, stop) hipEvent_t pair that
+        the bucket's kernel records its own start and end into."""
+        main, aux, handles = self._fanout(stream, self.gather_streams)
+        lib = zs.lib()
         for bi in range(len(self._g)):
-            self.gather(bi, s)
+            if timer is not None:
+                lib.zs3_time_next_launch(*timer())
+            self.gather(bi, handles[bi % len(handles)])
+        self._join(main, aux)
 
     def reduce_scatter(self, stream=None):
         """Every gradient bucket, fanned out over the main and auxiliary
         streams and joined back into the main stream."""
-        torch = self.torch
-        main = torch.cuda.current_stream() if stream is None else stream
-        streams = [main] + self.aux_streams
-        if len(streams) > 1:
-            self._fork.record(main)
-            for a in self.aux_streams:
-                a.wait_event(self._fork)
-        handles = [int(x.cuda_stream) for x in streams]
+        main, aux, handles = self._fanout(stream, self.rs_streams)
         lib = zs.lib()
         for i, (n, ids, src) in enumerate(self._r):
             self._ok(lib.zs3_reduce_scatter_local(self.h, self.rank, self.dcode, n, ids, src,
                                                   self.grad.data_ptr(), handles[i % len(handles)]))
-        for a, e in zip(self.aux_streams, self._joins):
-            e.record(a)
-            main.wait_event(e)
+        self._join(main, aux)
 
     def repartition(self, stream=None):
         n, ids, ptrs = self._p
@@ -227,15 +249,15 @@ class ShardStep:
                                             self.grad.data_ptr(), self.shard.data_ptr(), self.scale_ptr,
                                             self.flag_ptr, ctypes.byref(hp), s))
 
-    def step(self, stream=None, on_phase=None):
+    def step(self, stream=None, on_phase=None, gather_timer=None):
         """One whole shard step; ``on_phase(name)`` is called before each phase
         and with None at the end (for event timing)."""
         self.t += 1
         mark = on_phase or (lambda name: None)
         mark("gather_fwd")
-        self.gather_pass(stream)
+        self.gather_pass(stream, gather_timer)
         mark("gather_bwd")
-        self.gather_pass(stream)
+        self.gather_pass(stream, gather_timer)
         mark("reduce_scatter")
         self.reduce_scatter(stream)
         mark("partition")
