@@ -317,7 +317,7 @@ def main():
     gather_bytes = nbytes["pack"] + nbytes["unpack"]
     per_launch_bytes = gather_bytes / (2 * len(step.gather_buckets))
     achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
-    roofline = {"kernel": "gather: pack + unpack of one bucket (k_copy<4>)", "bound": "hbm",
+    roofline = {"kernel": "gather: pack + unpack of one bucket (k_copy_inline<4>)", "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_entry(cfg.name),
                 "launches": launches, "avg_launch_ms": round(avg_ms, 5),
