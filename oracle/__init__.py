@@ -24,7 +24,8 @@ Pages cited (short tags used in every docstring here):
 Modules:
 
 * ``zero3``  -- the oracle proper: layout, partition, gather pack/unpack,
-  reduce-scatter, shard-aware grad norm, fused Adam + cast.
+  reduce-scatter (contiguous path, and the non-contiguous path's send-side
+  pack and owner-side reduce), shard-aware grad norm, fused Adam + cast.
 * ``brute``  -- pure-Python per-element loops for tiny inputs, used only to
   pin ``zero3`` (a second, differently structured derivation).
 
@@ -54,6 +55,8 @@ from .zero3 import (  # noqa: F401
     partition,
     reduce_buckets,
     reduce_scatter,
+    scatter_pack,
+    scatter_reduce,
     sub_groups,
     to_f32,
     unpack,

@@ -311,6 +311,64 @@ def reduce_scatter(layout: Layout, rank: int, dtype: str, ds_ids: Sequence[int],
         grad_flat[o + (hi - lo):o + p.partition_size] = 0
 
 
+def scatter_pack(layout: Layout, ds_ids: Sequence[int],
+                 grads: Dict[int, np.ndarray]) -> List[np.ndarray]:
+    """One rank's send side of the non-contiguous gradient path.
+
+    [codex] 6.2, second row of the reduce-path table: without a contiguous
+    bucket the gradients go through reduce_scatter_coalesced, which
+    scatters straight to the owners.  Reading: the wire mirrors
+    all_gather_coalesced ([codex] 5.2, 7): the bucket's parameters in
+    ascending ds_id, each split into N partitions of partition_size
+    elements (zeros past numel); chunk d holds partition d of every
+    parameter back to back, so chunk d goes to rank d.  ``grads[ds_id]`` is
+    this rank's full flattened 16-bit gradient.  Persistent parameters are
+    never partitioned ([codex] 5.3) and take the all-reduce path instead.
+    Returns the N chunks.
+    """
+    slots = _bucket(layout, ds_ids, allow_persistent=False)
+    N = layout.world_size
+    chunks = []
+    for d in range(N):
+        parts = []
+        for p in slots:
+            g = np.asarray(grads[p.ds_id], np.uint16).reshape(-1)
+            assert g.size == p.numel
+            part = np.zeros(p.partition_size, dtype=np.uint16)
+            lo, hi = layout.own_range(p, d)
+            part[:hi - lo] = g[lo:hi]
+            parts.append(part)
+        chunks.append(np.concatenate(parts) if parts else np.zeros(0, np.uint16))
+    return chunks
+
+
+def scatter_reduce(layout: Layout, rank: int, dtype: str, ds_ids: Sequence[int],
+                   received: Sequence[np.ndarray], grad_flat: np.ndarray) -> None:
+    """The owner's side of the non-contiguous gradient path.
+
+    ``received[v]`` is chunk ``rank`` of virtual rank v's ``scatter_pack``
+    (what the reduce-scatter delivers from v).  Same arithmetic as
+    ``reduce_scatter`` ([codex] 6.2; [csdn] step 3): fp32 sum from +0 over
+    v = 0..N-1 in order, one fp32 division by N, round to the 16-bit type,
+    written at the parameter's place in the flat gradient buffer; padding
+    positions are written as 0 whatever the chunks hold there.
+    """
+    slots = _bucket(layout, ds_ids, allow_persistent=False)
+    N = layout.world_size
+    assert len(received) == N
+    c = 0
+    for p in slots:
+        lo, hi = layout.own_range(p, rank)
+        acc = np.zeros(hi - lo, dtype=np.float32)
+        for v in range(N):
+            acc = acc + to_f32(np.asarray(received[v], np.uint16)[c:c + (hi - lo)], dtype)
+        avg = acc / np.float32(N)
+        o = p.shard_offset
+        grad_flat[o:o + (hi - lo)] = from_f32(avg, dtype)
+        grad_flat[o + (hi - lo):o + p.partition_size] = 0
+        c += p.partition_size
+
+
 # --------------------------------------------------------------------------
 # a4: shard-aware global gradient norm and shared clip coefficient
 # --------------------------------------------------------------------------
