@@ -10,10 +10,14 @@ data-parallel ranks are N virtual ranks in this GPU's HBM; inputs are
 synthetic (seeded N(0, 0.02) weights, N(0, 1e-3) gradients with 1% x100
 outliers) and resident in HBM before timing starts.
 
-Prints ONE JSON line: effective HBM GB/s of the step (algorithmic bytes /
-time), its fraction of 8 TB/s and params/s, the roofline entry of the
-dominant kernel (unpack) timed with HIP events on the launch stream, and
-the CPU oracle timed on a bounded sample of the same workload.
+Prints ONE JSON line: effective HBM GB/s of the step (its fixed algorithmic
+byte budget / time: 2 x (pack + unpack) + reduce-scatter + re-partition +
+norm + Adam, the same for every variant, so a variant that fuses away a
+pass shows as less time for the same work; the bytes each variant actually
+has to move are reported beside it), its fraction of 8 TB/s and params/s,
+the roofline entry of the dominant kernel (the fused gather) timed with HIP
+events on the launch stream, and the CPU oracle timed on a bounded sample
+of the same workload.
 """
 
 from __future__ import annotations
@@ -49,6 +53,10 @@ def parse():
     ap.add_argument("--rs-streams", type=int, default=1, help="streams the gradient buckets are spread over")
     ap.add_argument("--gather-streams", type=int, default=1, help="streams the gather buckets are spread over")
     ap.add_argument("--no-kernel-timer", action="store_true", help="do not time the gather launches")
+    ap.add_argument("--fuse-norm", type=int, default=0, choices=(0, 1),
+                    help="1: the reduce-scatter also writes the norm's partial sums (no second read of grad_flat)")
+    ap.add_argument("--reduce-path", default="contiguous", choices=("contiguous", "coalesced"),
+                    help="gradient path: all-reduced buckets (default) or reduce_scatter_coalesced")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -111,14 +119,15 @@ class KernelTimer:
             self.hip.hipEventDestroy(self.ct.c_void_p(b))
 
 
-def make_step(cfg, rank, rs_streams=1, gather_streams=1):
+def make_step(cfg, rank, rs_streams=1, gather_streams=1, fuse_norm=False, reduce_path="contiguous"):
     from zero_sharded_state_amd.shard_step import AdamConfig, ShardStep
 
     return ShardStep(world_size=cfg.world_size, rank=rank, threshold=cfg.threshold, ds_ids=cfg.ds_ids,
                      numels=cfg.numels, dtype=cfg.dtype, prefetch_bucket_size=cfg.prefetch_bucket_size,
                      reduce_bucket_size=cfg.reduce_bucket_size, sub_group_size=cfg.sub_group_size,
                      adam=AdamConfig(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay),
-                     max_norm=cfg.max_norm, rs_streams=rs_streams, gather_streams=gather_streams)
+                     max_norm=cfg.max_norm, rs_streams=rs_streams, gather_streams=gather_streams,
+                     fuse_norm=fuse_norm, reduce_path=reduce_path)
 
 
 def fill_inputs(step, cfg):
@@ -133,6 +142,14 @@ def fill_inputs(step, cfg):
                         out=step.pers_full)
     device_normal16(step.N * step.S, cfg.grad_std, cfg.dtype, dev, (cfg.seed, cfg.config_id, KIND_GRAD, step.rank),
                     outlier_prob=cfg.outlier_prob, outlier_mult=cfg.outlier_mult, out=step.recv)
+    if step.reduce_path == "coalesced":
+        # the rank's own full gradients and the chunks its peers send it
+        device_normal16(step.own_grads.numel(), cfg.grad_std, cfg.dtype, dev,
+                        (cfg.seed, cfg.config_id, KIND_GRAD, 1000 + step.rank), outlier_prob=cfg.outlier_prob,
+                        outlier_mult=cfg.outlier_mult, out=step.own_grads)
+        device_normal16(step.xbuf.numel(), cfg.grad_std, cfg.dtype, dev,
+                        (cfg.seed, cfg.config_id, KIND_GRAD, 2000 + step.rank), outlier_prob=cfg.outlier_prob,
+                        outlier_mult=cfg.outlier_mult, out=step.xbuf)
     step.init_from_full()
     step.reduce_scatter()
     step.fill_peer_norms()
@@ -244,7 +261,7 @@ def main():
     cfg = get_config(args.config)
     rank = cfg.bench_rank if args.rank is None else args.rank
     log(f"config {cfg.name}: {cfg.title}, rank {rank}")
-    step = make_step(cfg, rank, args.rs_streams, args.gather_streams)
+    step = make_step(cfg, rank, args.rs_streams, args.gather_streams, bool(args.fuse_norm), args.reduce_path)
     log(f"layout: S+P={step.S:,} own real={step.own_real:,} F={step.F:,} gather buckets={len(step.gather_buckets)} "
         f"reduce buckets={len(step.reduce_buckets)} sub-groups={len(step.sub_groups)}")
     t0 = time.time()
@@ -282,8 +299,9 @@ def main():
     log(f"timed {args.steps} steps in {wall:.3f} s")
 
     ms_per_step = wall * 1e3 / args.steps
-    nbytes = step.algorithmic_bytes()
-    total_bytes = sum(nbytes.values())
+    nbytes = step.algorithmic_bytes()          # what this variant of the step must move, per kernel
+    total_bytes = step.budget_bytes()          # the step's fixed budget (equal work for every variant)
+    moved_bytes = sum(nbytes.values())
     gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
     params_per_s = step.own_real / (ms_per_step * 1e-3)
 
@@ -294,7 +312,8 @@ def main():
             phases[name] = phases.get(name, 0.0) + e0.elapsed_time(e1)
     phase_bytes = {"gather_fwd": (nbytes["pack"] + nbytes["unpack"]) // 2,
                    "gather_bwd": (nbytes["pack"] + nbytes["unpack"]) // 2,
-                   "reduce_scatter": nbytes["reduce_scatter"], "partition": nbytes["partition"],
+                   "reduce_scatter": nbytes["reduce_scatter"] + nbytes.get("scatter_pack", 0),
+                   "partition": nbytes["partition"],
                    "grad_norm": nbytes["grad_norm"], "adam": nbytes["adam"]}
     per_step = sorted(evs[0][1].elapsed_time(evs[-1][1]) for evs in phase_events)
     step_stats = {"min": round(per_step[0], 4), "median": round(per_step[len(per_step) // 2], 4),
@@ -303,7 +322,7 @@ def main():
     for name, ms in phases.items():
         ms /= args.steps
         kernels[name] = {"ms": round(ms, 4), "bytes": phase_bytes[name],
-                         "GBps": round(phase_bytes[name] / (ms * 1e-3) / 1e9, 1)}
+                         "GBps": round(phase_bytes[name] / (ms * 1e-3) / 1e9, 1) if phase_bytes[name] else None}
 
     # Roofline entry of the dominant kernel: the fused gather (pack + unpack
     # of one bucket, k_copy<4>), average duration over the timed launches.
@@ -355,6 +374,7 @@ def main():
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "params_per_s": round(params_per_s, 1),
         "bytes_per_step": total_bytes,
+        "bytes_moved_per_step": moved_bytes,
         "config": {
             "workload": f"{cfg.title}: fused shard step of rank {rank} ({cfg.total_params:,} params, "
                         f"{step.own_real:,} own elements)",
@@ -363,6 +383,7 @@ def main():
             "gather_buckets": len(step.gather_buckets), "reduce_buckets": len(step.reduce_buckets),
             "sub_groups": len(step.sub_groups), "prefetch_bucket_size": cfg.prefetch_bucket_size,
             "reduce_bucket_size": cfg.reduce_bucket_size, "sub_group_size": cfg.sub_group_size,
+            "reduce_path": step.reduce_path, "fused_norm": step.fuse_norm,
         },
         "kernels": kernels,
         "roofline": roofline,

@@ -35,8 +35,9 @@
  *     reuse it.  Cached tables are freed only by zs3_layout_destroy, which
  *     first waits for the device to go idle.
  *   - Calls on one layout from several host threads must be serialised by
- *     the caller.  zs3_grad_norm keeps per-layout scratch: two norm calls
- *     on one layout that overlap on different streams race.
+ *     the caller.  zs3_grad_norm and zs3_grad_norm_partials keep
+ *     per-layout scratch: two norm calls on one layout that overlap on
+ *     different streams race.
  */
 #ifndef ZS3_H
 #define ZS3_H
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define ZS3_ABI_VERSION 1
+#define ZS3_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define ZS3_API __attribute__((visibility("default")))
@@ -63,14 +64,14 @@ enum {
     ZS3_EDTYPE = -2,     /* dtype is neither ZS3_FP16 nor ZS3_BF16 */
     ZS3_EDUPID = -3,     /* a ds_id appears twice */
     ZS3_ENOTFOUND = -4,  /* a ds_id is not in the layout */
-    ZS3_EPERSIST = -5,   /* a persistent (never partitioned) parameter in a gather request */
+    ZS3_EPERSIST = -5,   /* a persistent (never partitioned) parameter where only partitioned ones may be */
     ZS3_EALIAS = -6,     /* an output overlaps an input it must not overlap */
     ZS3_EHIP = -7,       /* a HIP runtime call or kernel launch failed */
     ZS3_ENOMEM = -8      /* host or device allocation failed */
 };
 
 enum { ZS3_FP16 = 1, ZS3_BF16 = 2 };          /* 16-bit storage types */
-enum { ZS3_PACK = 1, ZS3_UNPACK = 2 };        /* zs3_gather_coalesced modes (bit mask) */
+enum { ZS3_PACK = 1, ZS3_UNPACK = 2, ZS3_REDUCE = 4 };   /* gather / scatter modes (bit mask) */
 enum { ZS3_GATHER_BUCKETS = 1, ZS3_REDUCE_BUCKETS = 2 };
 
 typedef struct zs3_layout* zs3_layout_t;
@@ -243,7 +244,60 @@ ZS3_API zs3_status zs3_gather_coalesced(zs3_layout_t layout, int32_t rank, int32
  */
 ZS3_API zs3_status zs3_reduce_scatter_local(zs3_layout_t layout, int32_t rank, int32_t dtype, int32_t n,
                                     const int64_t* ds_ids, const void* const* src, void* grad_flat,
-                                    void* stream);
+                                    double* partials, void* stream);
+/* partials: NULL, or the rank's norm slot array (dev, n_slots doubles from
+ * zs3_layout_norm_slots).  When set, the same launch also writes, into the
+ * slots that belong to the n parameters, sums of x*x over the 16-bit values
+ * it writes (x widened exactly to double, sums in double), so that
+ * zs3_grad_norm_partials can form the norm without reading grad_flat again
+ * (the fusion of the norm's read into the reduce).  Each parameter owns a
+ * fixed range of slots (partitioned parameters first, then persistent
+ * ones), so calls for different buckets, on any streams, write disjoint
+ * slots; a call rewrites every slot of its parameters.  partials must not
+ * overlap grad_flat or the sources. */
+
+/* Norm slots of a layout: n_slots doubles in all, the first n_part_slots
+ * for partitioned parameters.  The same for every rank. */
+ZS3_API zs3_status zs3_layout_norm_slots(zs3_layout_t layout, int64_t* n_slots, int64_t* n_part_slots);
+
+/* ------------------------- (3b) non-contiguous path: reduce_scatter_coalesced
+ * [codex] 6.2, second gradient path: without a contiguous bucket, the
+ * gradients are reduce-scattered straight to their owners, and each owner's
+ * averaged interval lands in the flat gradient buffer as on the contiguous
+ * path.  Reading: the wire mirrors all_gather_coalesced ([codex] 5.2, 7):
+ * parameters in ascending ds_id whatever the request order, c_j = prefix
+ * sum of partition sizes, C = chunk_numel = sum of partition sizes.
+ *
+ * The bucket is the n parameters ds_ids (host, no duplicates, none
+ * persistent: persistent gradients are whole on every rank and take
+ * zs3_reduce_scatter_local, the all-reduce path).
+ *   mode & ZS3_PACK (the rank's send side):
+ *       send[d*C + c_j + k] = g_j[d*ps_j + k] when d*ps_j + k < numel_j,
+ *                             else 0,
+ *       for every destination rank d < N and k < ps_j.  grads: host array
+ *       of n dev pointers, grads[i] = this rank's full flattened gradient
+ *       of parameter ds_ids[i] (numel_i elements).  send: dev, N*C elements
+ *       (the reduce-scatter's rank-major input: chunk d goes to rank d).
+ *   mode & ZS3_REDUCE (the owner side, after the collective):
+ *       grad_flat[shard_offset_j + k] =
+ *           round16( (((0 + r_0[c_j+k]) + r_1[c_j+k]) + ... + r_{N-1}[c_j+k]) / N )
+ *       for k < hi_j - lo_j (the rank's real elements), 0 for the padding
+ *       positions k < ps_j whatever the chunks hold there; fp32 operations
+ *       as in zs3_reduce_scatter_local, so both paths give the same bits.
+ *       recv_chunks: host array of N dev pointers, recv_chunks[v] = the C
+ *       elements rank v sent to this rank (chunk `rank` of v's send
+ *       buffer).  grad_flat: dev, shard_numel elements.  partials: as in
+ *       zs3_reduce_scatter_local (NULL: no sums).  Fastest when every
+ *       recv_chunks[v] has the byte address of grad_flat + shard_offset of
+ *       the bucket's first parameter modulo 16.
+ * With both bits the pack runs first (recv_chunks[rank] may then point
+ * into send).  Unused pointers may be NULL.  Outputs must not overlap the
+ * inputs they are computed from.
+ */
+ZS3_API zs3_status zs3_reduce_scatter_coalesced(zs3_layout_t layout, int32_t rank, int32_t dtype, int32_t mode,
+                                        int32_t n, const int64_t* ds_ids, const void* const* grads, void* send,
+                                        const void* const* recv_chunks, void* grad_flat, double* partials,
+                                        void* stream);
 
 /* ------------------------------------------------ (4) global grad norm
  * [codex] 6.3: every sub-group is unscaled and clipped with the one global
@@ -268,6 +322,18 @@ ZS3_API zs3_status zs3_reduce_scatter_local(zs3_layout_t layout, int32_t rank, i
 ZS3_API zs3_status zs3_grad_norm(zs3_layout_t layout, int32_t rank, int32_t dtype, const void* grad_flat,
                          double* sumsq, int32_t finalize, double max_norm, double loss_scale,
                          double* norm_out, float* scale_out, int32_t* nonfinite, void* stream);
+
+/* The same partial and finalize steps from the norm slots that
+ * zs3_reduce_scatter_local / zs3_reduce_scatter_coalesced filled (every
+ * parameter of the layout must have been reduced with partials since its
+ * slots were last meant to change): sumsq[rank] = sum of the partitioned
+ * slots, sumsq[N] = sum of the persistent slots, both in a fixed order
+ * (the result is reproducible, and equal to zs3_grad_norm's up to the
+ * order of double additions).  partials: dev, n_slots doubles.  Other
+ * arguments as in zs3_grad_norm. */
+ZS3_API zs3_status zs3_grad_norm_partials(zs3_layout_t layout, int32_t rank, const double* partials,
+                                  double* sumsq, int32_t finalize, double max_norm, double loss_scale,
+                                  double* norm_out, float* scale_out, int32_t* nonfinite, void* stream);
 
 /* ----------------------------------------- (5) fused Adam + 16-bit cast
  * [codex] 6.3: per sub-group, the rank's fp32 partition is stepped by the

@@ -28,11 +28,11 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     syms = _declared_symbols()
-    assert len(syms) == 18
+    assert len(syms) == 21
     assert sorted(zs.EXPORTS) == syms
     for s in syms:
         assert hasattr(L, s), s
-    assert zs.zs3_abi_version() == 1
+    assert zs.zs3_abi_version() == 2
     assert zs.zs3_status_str(-5).startswith("persistent")
 
 
@@ -149,6 +149,28 @@ def test_call_validation_enqueues_nothing():
                                                      base + (3 << 20), base + (4 << 20), base + (5 << 20), None,
                                                      {"lr": 1e-3, "beta1": .9, "beta2": .999, "eps": 1e-8, "step": 1},
                                                      stream=0)),
+            (zs.ZS3_EPERSIST, lambda: zs.zs3_reduce_scatter_coalesced(h, 0, "bf16", zs.ZS3_PACK, [0, 1],
+                                                                      grads=[base, base + 4096], send=base + 8192,
+                                                                      stream=0)),
+            (zs.ZS3_EINVAL, lambda: zs.zs3_reduce_scatter_coalesced(h, 0, "bf16", zs.ZS3_UNPACK, [0],
+                                                                    grads=[base], send=base + 8192, stream=0)),
+            (zs.ZS3_EINVAL, lambda: zs.zs3_reduce_scatter_coalesced(h, 0, "bf16", zs.ZS3_PACK, [0],
+                                                                    grads=None, send=base + 8192, stream=0)),
+            (zs.ZS3_EALIAS, lambda: zs.zs3_reduce_scatter_coalesced(h, 0, "bf16", zs.ZS3_PACK, [0],
+                                                                    grads=[base], send=base + 100, stream=0)),
+            (zs.ZS3_EALIAS, lambda: zs.zs3_reduce_scatter_coalesced(h, 0, "bf16", zs.ZS3_REDUCE, [0, 2],
+                                                                    recv_chunks=[base + 4096 * k for k in range(4)],
+                                                                    grad_flat=base + 4096 * 3 - 2, stream=0)),
+            (zs.ZS3_EINVAL, lambda: zs.zs3_reduce_scatter_coalesced(h, 0, "bf16", zs.ZS3_REDUCE, [0],
+                                                                    recv_chunks=[base + 4096 * k for k in range(4)],
+                                                                    grad_flat=base + 65536, partials=base + 65536 * 2 + 4,
+                                                                    stream=0)),
+            (zs.ZS3_EALIAS, lambda: zs.zs3_reduce_scatter_local(h, 0, "bf16", [0], [base + 4096 * k for k in range(4)],
+                                                                base + 65536, partials=base + 65536 + 8, stream=0)),
+            (zs.ZS3_EINVAL, lambda: zs.zs3_grad_norm_partials(h, 0, base + 4, base + 8192, False, stream=0)),
+            (zs.ZS3_EINVAL, lambda: zs.zs3_grad_norm_partials(h, 0, base, base + 1 << 20, True, 0.0, 1.0,
+                                                              base + 8192, base + 8200, base + 8204, stream=0)),
+            (zs.ZS3_EALIAS, lambda: zs.zs3_grad_norm_partials(h, 0, base, base + 8, False, stream=0)),
         ]
         for want, call in cases:
             with pytest.raises(zs.Zs3Error) as e:
@@ -158,5 +180,25 @@ def test_call_validation_enqueues_nothing():
         # an empty request is a no-op, not an error
         zs.zs3_partition(h, 0, "fp16", [], [], base, stream=0)
         assert zs.zs3_gather_coalesced(h, 0, "fp16", zs.ZS3_PACK, [], base, base + 4096, stream=0) == []
+        zs.zs3_reduce_scatter_coalesced(h, 0, "fp16", zs.ZS3_PACK | zs.ZS3_REDUCE, [], grads=[], send=base,
+                                        recv_chunks=[base] * 4, grad_flat=base + 65536, stream=0)
+    finally:
+        zs.zs3_layout_destroy(h)
+
+
+def _slot_count(ps_list, piece=256 * 8 * 8, sub=8):
+    return sum(sub * (1 if ps <= piece else -(-ps // piece)) for ps in ps_list)
+
+
+@pytest.mark.parametrize("name", sorted(CONFIGS))
+def test_norm_slots_cover_every_parameter(name):
+    """One group of workgroup slots per reduce-scatter piece of each
+    parameter's partition, partitioned parameters first."""
+    cfg = get_config(name)
+    h, ol = _both(name)
+    try:
+        n_slots, n_part = zs.zs3_layout_norm_slots(h)
+        assert n_part == _slot_count([p.partition_size for p in ol.params if not p.persistent])
+        assert n_slots == n_part + _slot_count([p.partition_size for p in ol.params if p.persistent])
     finally:
         zs.zs3_layout_destroy(h)

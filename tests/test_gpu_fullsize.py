@@ -5,7 +5,8 @@ over four streams).
 * c2 (GPT-2-small set) and c3 (one Llama-3-8B layer): the whole step chained
   for 10 steps on the GPU against the oracle's own 10-step chain from the
   same synthetic inputs (weights, per-step gradients, the peers' norm
-  partials); every output compared.
+  partials); every output compared.  Variants: the norm fused into the
+  reduce, and the non-contiguous gradient path (reduce_scatter_coalesced).
 * c4 (Llama-3-8B set, 8.03B parameters, rank 0) and c5 (ragged 7.46B set,
   N = 64, rank 63, fp16, misaligned): each call fed fresh synthetic inputs,
   its outputs checked on a sample of whole parameters (the oracle recomputes
@@ -35,13 +36,13 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-def _step(cfg, rank):
+def _step(cfg, rank, fuse_norm=False, reduce_path="contiguous"):
     from zero_sharded_state_amd.shard_step import AdamConfig, ShardStep
     return ShardStep(world_size=cfg.world_size, rank=rank, threshold=cfg.threshold, ds_ids=cfg.ds_ids,
                      numels=cfg.numels, dtype=cfg.dtype, prefetch_bucket_size=cfg.prefetch_bucket_size,
                      reduce_bucket_size=cfg.reduce_bucket_size, sub_group_size=cfg.sub_group_size,
                      adam=AdamConfig(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay),
-                     max_norm=cfg.max_norm, rs_streams=4)
+                     max_norm=cfg.max_norm, rs_streams=4, fuse_norm=fuse_norm, reduce_path=reduce_path)
 
 
 def h16(t):
@@ -74,14 +75,40 @@ def _recv_grads(step, L, host_recv):
 # c2 / c3: the whole step, chained, 10 steps
 # --------------------------------------------------------------------------
 
+def _oracle_reduce(step, L, cfg, rank, host_recv, host_own=None, host_x=None):
+    """The oracle's flat gradient of one step.  Contiguous path: from the
+    received slices.  Non-contiguous path: partitioned parameters from the
+    N chunks addressed to this rank (its own packed by the oracle, the
+    peers' as the GPU held them), persistent ones from the slices."""
+    gf = np.zeros(L.shard_numel, np.uint16)
+    grads = _recv_grads(step, L, host_recv)
+    for bi, b in enumerate(oracle.reduce_buckets(L, cfg.reduce_bucket_size)):
+        if step.reduce_path == "contiguous":
+            oracle.reduce_scatter(L, rank, cfg.dtype, b, grads, gf)
+            continue
+        ids_part, ids_pers, C, _, chunks = step.coalesced[bi]
+        assert sorted(ids_part + ids_pers) == sorted(b)
+        if ids_part:
+            own = {d: host_own[step.grad_off[d]:step.grad_off[d] + L.slot(d).numel] for d in ids_part}
+            recv = [oracle.scatter_pack(L, ids_part, own)[rank] if v == rank else
+                    host_x[chunks[v]:chunks[v] + C] for v in range(step.N)]
+            oracle.scatter_reduce(L, rank, cfg.dtype, ids_part, recv, gf)
+        if ids_pers:
+            oracle.reduce_scatter(L, rank, cfg.dtype, ids_pers, grads, gf)
+    return gf
+
+
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,rank", [("c2", 0), ("c2", 7), ("c3", 0), ("c3", 7)])
-def test_chained_steps_match_oracle(name, rank):
+@pytest.mark.parametrize("name,rank,fuse_norm,reduce_path", [
+    ("c2", 0, False, "contiguous"), ("c2", 7, False, "contiguous"), ("c3", 0, False, "contiguous"),
+    ("c3", 7, False, "contiguous"), ("c2", 3, True, "contiguous"), ("c2", 7, True, "coalesced"),
+    ("c3", 0, True, "coalesced")])
+def test_chained_steps_match_oracle(name, rank, fuse_norm, reduce_path):
     import torch
     cfg = get_config(name)
     N, dt = cfg.world_size, cfg.dtype
-    note(f"chain {name} rank={rank}: set-up")
-    step = _step(cfg, rank)
+    note(f"chain {name} rank={rank} fuse_norm={fuse_norm} {reduce_path}: set-up")
+    step = _step(cfg, rank, fuse_norm, reduce_path)
     L = oracle.make_layout(N, cfg.threshold, cfg.ds_ids, cfg.numels)
     try:
         full = {d: weights_host(cfg, d) for d in cfg.ds_ids}
@@ -105,6 +132,15 @@ def test_chained_steps_match_oracle(name, rank):
             device_normal16(step.N * step.S, cfg.grad_std, dt, step.device, (cfg.seed, cfg.config_id, KIND_GRAD, t),
                             outlier_prob=cfg.outlier_prob, outlier_mult=cfg.outlier_mult, out=step.recv)
             host_recv = h16(step.recv)
+            host_own = host_x = None
+            if reduce_path == "coalesced":
+                device_normal16(step.own_grads.numel(), cfg.grad_std, dt, step.device,
+                                (cfg.seed, cfg.config_id, KIND_GRAD, 100 + t), outlier_prob=cfg.outlier_prob,
+                                outlier_mult=cfg.outlier_mult, out=step.own_grads)
+                device_normal16(step.xbuf.numel(), cfg.grad_std, dt, step.device,
+                                (cfg.seed, cfg.config_id, KIND_GRAD, 200 + t), outlier_prob=cfg.outlier_prob,
+                                outlier_mult=cfg.outlier_mult, out=step.xbuf)
+                host_own, host_x = h16(step.own_grads), h16(step.xbuf)
             # GPU: the step as bench.py runs it, with the peers' partial sums supplied
             step.t = t - 1
             step.gather_pass()
@@ -116,10 +152,7 @@ def test_chained_steps_match_oracle(name, rank):
             step.adam_step(t)
             step.t = t
             # oracle chain
-            gf = np.zeros(L.shard_numel, np.uint16)
-            grads = _recv_grads(step, L, host_recv)
-            for b in oracle.reduce_buckets(L, cfg.reduce_bucket_size):
-                oracle.reduce_scatter(L, rank, dt, b, grads, gf)
+            gf = _oracle_reduce(step, L, cfg, rank, host_recv, host_own, host_x)
             a, q = oracle.grad_norm_partial(L, rank, dt, gf)
             parts = list(peers)
             parts[rank] = a

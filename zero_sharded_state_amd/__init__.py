@@ -31,6 +31,7 @@ ZS3_FP16 = 1
 ZS3_BF16 = 2
 ZS3_PACK = 1
 ZS3_UNPACK = 2
+ZS3_REDUCE = 4
 ZS3_GATHER_BUCKETS = 1
 ZS3_REDUCE_BUCKETS = 2
 
@@ -42,7 +43,8 @@ EXPORTS = (
     "zs3_layout_create", "zs3_layout_destroy", "zs3_layout_info", "zs3_layout_param_at",
     "zs3_layout_param", "zs3_layout_own_range", "zs3_plan_buckets", "zs3_sub_groups",
     "zs3_bucket_sizes", "zs3_partition", "zs3_gather_coalesced", "zs3_reduce_scatter_local",
-    "zs3_grad_norm", "zs3_adam_step",
+    "zs3_layout_norm_slots", "zs3_reduce_scatter_coalesced", "zs3_grad_norm", "zs3_grad_norm_partials",
+    "zs3_adam_step",
 )
 
 
@@ -88,7 +90,12 @@ _SIGNATURES = {
     "zs3_gather_coalesced": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _p_i64, _c_p, _c_p,
                                       ctypes.POINTER(_c_p), _c_p, _p_i64, _c_p]),
     "zs3_reduce_scatter_local": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _p_i64, ctypes.POINTER(_c_p),
-                                          _c_p, _c_p]),
+                                          _c_p, _c_p, _c_p]),
+    "zs3_layout_norm_slots": (_c_i32, [_c_p, _p_i64, _p_i64]),
+    "zs3_reduce_scatter_coalesced": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _p_i64, ctypes.POINTER(_c_p),
+                                              _c_p, ctypes.POINTER(_c_p), _c_p, _c_p, _c_p]),
+    "zs3_grad_norm_partials": (_c_i32, [_c_p, _c_i32, _c_p, _c_p, _c_i32, ctypes.c_double, ctypes.c_double,
+                                        _c_p, _c_p, _c_p, _c_p]),
     "zs3_grad_norm": (_c_i32, [_c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, ctypes.c_double,
                                ctypes.c_double, _c_p, _c_p, _c_p, _c_p]),
     "zs3_adam_step": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
@@ -266,9 +273,26 @@ def zs3_gather_coalesced(layout: int, rank: int, dtype, mode: int, ds_ids: Seque
 
 
 def zs3_reduce_scatter_local(layout: int, rank: int, dtype, ds_ids: Sequence[int], src: Sequence,
-                             grad_flat, stream=None) -> None:
+                             grad_flat, partials=None, stream=None) -> None:
     _check(lib().zs3_reduce_scatter_local(layout, rank, _dtype(dtype), len(ds_ids), _i64s(ds_ids), _ptrs(src),
-                                          _ptr(grad_flat), _stream(stream)))
+                                          _ptr(grad_flat), _ptr(partials), _stream(stream)))
+
+
+def zs3_layout_norm_slots(layout: int) -> Tuple[int, int]:
+    """(n_slots, n_part_slots) of the layout's norm slot array."""
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().zs3_layout_norm_slots(layout, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def zs3_reduce_scatter_coalesced(layout: int, rank: int, dtype, mode: int, ds_ids: Sequence[int],
+                                 grads: Optional[Sequence] = None, send=None,
+                                 recv_chunks: Optional[Sequence] = None, grad_flat=None, partials=None,
+                                 stream=None) -> None:
+    g = _ptrs(grads) if grads is not None else None
+    r = _ptrs(recv_chunks) if recv_chunks is not None else None
+    _check(lib().zs3_reduce_scatter_coalesced(layout, rank, _dtype(dtype), mode, len(ds_ids), _i64s(ds_ids), g,
+                                              _ptr(send), r, _ptr(grad_flat), _ptr(partials), _stream(stream)))
 
 
 def zs3_grad_norm(layout: int, rank: int, dtype, grad_flat, sumsq, finalize: bool, max_norm: float = 1.0,
@@ -276,6 +300,14 @@ def zs3_grad_norm(layout: int, rank: int, dtype, grad_flat, sumsq, finalize: boo
     _check(lib().zs3_grad_norm(layout, rank, _dtype(dtype), _ptr(grad_flat), _ptr(sumsq), int(bool(finalize)),
                                float(max_norm), float(loss_scale), _ptr(norm_out), _ptr(scale_out),
                                _ptr(nonfinite), _stream(stream)))
+
+
+def zs3_grad_norm_partials(layout: int, rank: int, partials, sumsq, finalize: bool, max_norm: float = 1.0,
+                           loss_scale: float = 1.0, norm_out=None, scale_out=None, nonfinite=None,
+                           stream=None) -> None:
+    _check(lib().zs3_grad_norm_partials(layout, rank, _ptr(partials), _ptr(sumsq), int(bool(finalize)),
+                                        float(max_norm), float(loss_scale), _ptr(norm_out), _ptr(scale_out),
+                                        _ptr(nonfinite), _stream(stream)))
 
 
 def zs3_adam_step(layout: int, rank: int, dtype, begin: int, end: int, master, exp_avg, exp_avg_sq, grad_flat,

@@ -110,7 +110,10 @@ struct Plan {
     T* at(size_t off) const { return reinterpret_cast<T*>(static_cast<char*>(dev) + off); }
 };
 
-enum Op : int64_t { kOpPartition = 1, kOpPack, kOpUnpack, kOpReduce, kOpNorm, kOpAdam, kOpGather };
+enum Op : int64_t {
+    kOpPartition = 1, kOpPack, kOpUnpack, kOpReduce, kOpNorm, kOpAdam, kOpGather, kOpScatterPack,
+    kOpScatterReduce, kOpNormSlots
+};
 
 constexpr size_t kMaxPlans = 1 << 14;
 
@@ -122,6 +125,8 @@ struct zs3_layout {
     std::vector<Slot> params;                       // ascending ds_id
     std::unordered_map<int64_t, int32_t> index;     // ds_id -> position
     int64_t shard_numel = 0;
+    std::vector<int64_t> slot_base;                 // first norm slot of each parameter (layout order)
+    int64_t n_slots = 0, n_part_slots = 0;
     std::unordered_map<Key, Plan, KeyHash> plans;
 
     ~zs3_layout() { release_plans(); }
@@ -336,6 +341,83 @@ Plan* find_plan(zs3_layout* L, const Key& k) {
     return it == L->plans.end() ? nullptr : &it->second;
 }
 
+// ---- reduce-scatter plans (both gradient paths) ----------------------------
+
+zs3_status build_rs_plan(zs3_layout* L, Key&& key, const std::vector<RsSeg>& segs,
+                         const std::vector<const uint16_t*>& srcs, int32_t N, Plan** out) {
+    std::vector<Piece> pieces;
+    bool co = true;
+    for (size_t i = 0; i < segs.size(); ++i) {
+        add_pieces(&pieces, static_cast<int32_t>(i), reinterpret_cast<uintptr_t>(segs[i].dst), segs[i].total, kRsPiece);
+        for (int32_t v = 0; v < N; ++v) {
+            const uint16_t* q = srcs[segs[i].src_index + v];
+            if (q != nullptr && ((reinterpret_cast<uintptr_t>(q) ^ reinterpret_cast<uintptr_t>(segs[i].dst)) & 15u) != 0)
+                co = false;
+        }
+    }
+    zs3_status s = check_grid(static_cast<int64_t>(pieces.size()), kRsSub);
+    if (s != ZS3_OK) return s;
+    Plan np;
+    np.n_pieces = static_cast<int64_t>(pieces.size());
+    np.co_aligned = co;
+    if (segs.size() <= static_cast<size_t>(kRsInlineSegs) &&
+        segs.size() * static_cast<size_t>(N) <= static_cast<size_t>(kRsInlineSrcs)) {
+        auto ri = std::make_shared<RsInline>();
+        std::memset(ri.get(), 0, sizeof(RsInline));
+        ri->nseg = static_cast<int32_t>(segs.size());
+        ri->world = N;
+        std::vector<int32_t> per_seg(segs.size(), 0);
+        for (const Piece& pc : pieces) ++per_seg[pc.seg];
+        int32_t npc = 0;
+        for (size_t i = 0; i < segs.size(); ++i) {
+            ri->piece_start[i] = npc;
+            npc += per_seg[i];
+            ri->head[i] = static_cast<int32_t>(((16u - (reinterpret_cast<uintptr_t>(segs[i].dst) & 15u)) & 15u) >> 1);
+            ri->dst[i] = segs[i].dst;
+            ri->real[i] = segs[i].real;
+            ri->total[i] = segs[i].total;
+            ri->slot[i] = segs[i].slot;
+            for (int32_t v = 0; v < N; ++v) ri->src[i * N + v] = srcs[segs[i].src_index + v];
+        }
+        ri->piece_start[segs.size()] = npc;
+        np.rs_inline = std::move(ri);
+    } else {
+        std::vector<size_t> offs;
+        s = upload(&np,
+                   {{segs.data(), segs.size() * sizeof(RsSeg)},
+                    {pieces.data(), pieces.size() * sizeof(Piece)},
+                    {srcs.data(), srcs.size() * sizeof(const uint16_t*)}},
+                   0, &offs);
+        if (s != ZS3_OK) return s;
+        np.off_segs = offs[0];
+        np.off_pieces = offs[1];
+        np.off_srcs = offs[2];
+    }
+    return store_plan(L, std::move(key), std::move(np), out);
+}
+
+zs3_status run_rs(RsPath path, const Plan* plan, int32_t dtype, int32_t N, double* partials, void* stream) {
+    if (plan->rs_inline)
+        return hip_status(launch_reduce_scatter_inline(path, dtype, *plan->rs_inline, plan->co_aligned, partials,
+                                                       static_cast<hipStream_t>(stream)),
+                          "reduce-scatter kernel launch");
+    return hip_status(launch_reduce_scatter(path, dtype, plan->at<RsSeg>(plan->off_segs),
+                                            plan->at<Piece>(plan->off_pieces), plan->n_pieces,
+                                            plan->at<const uint16_t*>(plan->off_srcs), N, plan->co_aligned, partials,
+                                            static_cast<hipStream_t>(stream)),
+                      "reduce-scatter kernel launch");
+}
+
+// The fused sums of squares need the layout's whole slot array, 8-byte
+// aligned and apart from the gradient buffer.
+zs3_status check_partials(const zs3_layout* L, const double* partials, const void* grad_flat) {
+    if (partials == nullptr) return ZS3_OK;
+    if (!aligned(partials, 8)) return fail(ZS3_EINVAL, "partials is not 8-byte aligned");
+    if (overlap(partials, 8 * L->n_slots, grad_flat, 2 * L->shard_numel))
+        return fail(ZS3_EALIAS, "partials overlaps grad_flat");
+    return ZS3_OK;
+}
+
 }  // namespace
 
 // ======================================================================
@@ -353,7 +435,7 @@ const char* zs3_status_str(zs3_status s) {
         case ZS3_EDTYPE: return "unsupported dtype";
         case ZS3_EDUPID: return "duplicate ds_id";
         case ZS3_ENOTFOUND: return "ds_id not in layout";
-        case ZS3_EPERSIST: return "persistent parameter in a gather request";
+        case ZS3_EPERSIST: return "persistent parameter in a request for partitioned ones";
         case ZS3_EALIAS: return "overlapping input and output";
         case ZS3_EHIP: return "HIP error";
         case ZS3_ENOMEM: return "out of memory";
@@ -403,6 +485,19 @@ zs3_status zs3_layout_create(int32_t world_size, int64_t persistence_threshold, 
         L->params.push_back(s);
     }
     L->shard_numel = offset;
+    // norm slots: partitioned parameters first, then persistent ones
+    L->slot_base.assign(L->params.size(), 0);
+    int64_t slot = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+        for (size_t k = 0; k < L->params.size(); ++k) {
+            const Slot& p = L->params[k];
+            if (p.persistent != (pass == 1)) continue;
+            L->slot_base[k] = slot;
+            slot += kRsSub * norm_slot_groups(p.ps);
+        }
+        if (pass == 0) L->n_part_slots = slot;
+    }
+    L->n_slots = slot;
     *out = L.release();
     return ok();
 }
@@ -700,7 +795,7 @@ zs3_status zs3_gather_coalesced(zs3_layout_t L, int32_t rank, int32_t dtype, int
 // ---------------------------------------------------------------- (3)
 
 zs3_status zs3_reduce_scatter_local(zs3_layout_t L, int32_t rank, int32_t dtype, int32_t n, const int64_t* ds_ids,
-                                    const void* const* src, void* grad_flat, void* stream) {
+                                    const void* const* src, void* grad_flat, double* partials, void* stream) {
     zs3_status s = check_layout_rank(L, rank);
     if (s != ZS3_OK) return s;
     if ((s = check_dtype(dtype)) != ZS3_OK) return s;
@@ -709,6 +804,7 @@ zs3_status zs3_reduce_scatter_local(zs3_layout_t L, int32_t rank, int32_t dtype,
     if (n == 0) return ok();
     if (src == nullptr) return fail(ZS3_EINVAL, "src is NULL");
     if ((s = check_ptr16(grad_flat, "grad_flat")) != ZS3_OK) return s;
+    if ((s = check_partials(L, partials, grad_flat)) != ZS3_OK) return s;
     const int32_t N = L->world;
     uint16_t* gbase = static_cast<uint16_t*>(grad_flat);
     for (int32_t i = 0; i < n; ++i) {
@@ -723,6 +819,8 @@ zs3_status zs3_reduce_scatter_local(zs3_layout_t L, int32_t rank, int32_t dtype,
                 if (overlap(q, 2 * real, gbase + o.offset, 2 * o.ps))
                     return fail(ZS3_EALIAS, "src[%d*N+%d] overlaps the written part of grad_flat", i, v);
             }
+            if (partials != nullptr && overlap(q, 2 * real, partials, 8 * L->n_slots))
+                return fail(ZS3_EALIAS, "src[%d*N+%d] overlaps partials", i, v);
         }
     }
     Key key{{kOpReduce, device_id(), rank, reinterpret_cast<int64_t>(grad_flat)}};
@@ -734,68 +832,115 @@ zs3_status zs3_reduce_scatter_local(zs3_layout_t L, int32_t rank, int32_t dtype,
     if (plan == nullptr) {
         std::vector<RsSeg> segs;
         std::vector<const uint16_t*> srcs;
-        std::vector<Piece> pieces;
-        bool co = true;
         for (int32_t k : order) {
             const Slot& p = L->params[pos[k]];
             const int64_t real = p.real(rank);
-            uint16_t* dst = gbase + p.offset;
-            const int32_t si = static_cast<int32_t>(segs.size());
-            segs.push_back(RsSeg{dst, real, p.ps, static_cast<int64_t>(srcs.size())});
-            for (int32_t v = 0; v < N; ++v) {
-                const uint16_t* q = static_cast<const uint16_t*>(src[static_cast<int64_t>(k) * N + v]);
-                if (real == 0) q = nullptr;
-                srcs.push_back(q);
-                if (q != nullptr && ((reinterpret_cast<uintptr_t>(q) ^ reinterpret_cast<uintptr_t>(dst)) & 15u) != 0) co = false;
-            }
-            add_pieces(&pieces, si, reinterpret_cast<uintptr_t>(dst), p.ps, kRsPiece);
+            segs.push_back(RsSeg{gbase + p.offset, real, p.ps, static_cast<int64_t>(srcs.size()), L->slot_base[pos[k]]});
+            for (int32_t v = 0; v < N; ++v)
+                srcs.push_back(real == 0 ? nullptr : static_cast<const uint16_t*>(src[static_cast<int64_t>(k) * N + v]));
         }
-        if ((s = check_grid(static_cast<int64_t>(pieces.size()), kRsSub)) != ZS3_OK) return s;
-        Plan np;
-        np.n_pieces = static_cast<int64_t>(pieces.size());
-        np.co_aligned = co;
-        if (segs.size() <= static_cast<size_t>(kRsInlineSegs) &&
-            segs.size() * static_cast<size_t>(N) <= static_cast<size_t>(kRsInlineSrcs)) {
-            auto ri = std::make_shared<RsInline>();
-            std::memset(ri.get(), 0, sizeof(RsInline));
-            ri->nseg = static_cast<int32_t>(segs.size());
-            ri->world = N;
-            std::vector<int32_t> per_seg(segs.size(), 0);
-            for (const Piece& pc : pieces) ++per_seg[pc.seg];
-            int32_t npc = 0;
-            for (size_t i = 0; i < segs.size(); ++i) {
-                ri->piece_start[i] = npc;
-                npc += per_seg[i];
-                ri->head[i] = static_cast<int32_t>(((16u - (reinterpret_cast<uintptr_t>(segs[i].dst) & 15u)) & 15u) >> 1);
-                ri->dst[i] = segs[i].dst;
-                ri->real[i] = segs[i].real;
-                ri->total[i] = segs[i].total;
-                for (int32_t v = 0; v < N; ++v) ri->src[i * N + v] = srcs[segs[i].src_index + v];
-            }
-            ri->piece_start[segs.size()] = npc;
-            np.rs_inline = std::move(ri);
-        } else {
-            std::vector<size_t> offs;
-            s = upload(&np,
-                       {{segs.data(), segs.size() * sizeof(RsSeg)},
-                        {pieces.data(), pieces.size() * sizeof(Piece)},
-                        {srcs.data(), srcs.size() * sizeof(const uint16_t*)}},
-                       0, &offs);
-            if (s != ZS3_OK) return s;
-            np.off_segs = offs[0];
-            np.off_pieces = offs[1];
-            np.off_srcs = offs[2];
-        }
-        store_plan(L, std::move(key), std::move(np), &plan);
+        if ((s = build_rs_plan(L, std::move(key), segs, srcs, N, &plan)) != ZS3_OK) return s;
     }
-    if (plan->rs_inline)
-        return hip_status(launch_reduce_scatter_inline(dtype, *plan->rs_inline, plan->co_aligned,
-                                                       static_cast<hipStream_t>(stream)),
-                          "reduce-scatter kernel launch");
-    return hip_status(launch_reduce_scatter(dtype, plan->at<RsSeg>(plan->off_segs), plan->at<Piece>(plan->off_pieces),
-                                            plan->n_pieces, plan->at<const uint16_t*>(plan->off_srcs), N,
-                                            plan->co_aligned, static_cast<hipStream_t>(stream)),
-                      "reduce-scatter kernel launch");
+    return run_rs(kRsContiguous, plan, dtype, N, partials, stream);
+}
+
+zs3_status zs3_reduce_scatter_coalesced(zs3_layout_t L, int32_t rank, int32_t dtype, int32_t mode, int32_t n,
+                                        const int64_t* ds_ids, const void* const* grads, void* send,
+                                        const void* const* recv_chunks, void* grad_flat, double* partials,
+                                        void* stream) {
+    zs3_status s = check_layout_rank(L, rank);
+    if (s != ZS3_OK) return s;
+    if ((s = check_dtype(dtype)) != ZS3_OK) return s;
+    if (mode != ZS3_PACK && mode != ZS3_REDUCE && mode != (ZS3_PACK | ZS3_REDUCE))
+        return fail(ZS3_EINVAL, "mode %d is not PACK, REDUCE or both", mode);
+    std::vector<int32_t> pos, order;
+    if ((s = resolve(L, n, ds_ids, false, &pos, &order)) != ZS3_OK) return s;
+    const int32_t N = L->world;
+    std::vector<int64_t> c(n);
+    int64_t chunk = 0;
+    for (int32_t k : order) {
+        c[k] = chunk;
+        chunk += L->params[pos[k]].ps;
+    }
+    const bool do_pack = (mode & ZS3_PACK) != 0, do_reduce = (mode & ZS3_REDUCE) != 0;
+    uint16_t* gbase = static_cast<uint16_t*>(grad_flat);
+    if (do_pack) {
+        if (n > 0 && grads == nullptr) return fail(ZS3_EINVAL, "grads is NULL");
+        if ((s = check_ptr16(send, "send")) != ZS3_OK) return s;
+        for (int32_t i = 0; i < n; ++i) {
+            if ((s = check_ptr16(grads[i], "grads[i]")) != ZS3_OK) return s;
+            if (overlap(grads[i], 2 * L->params[pos[i]].numel, send, 2 * N * chunk))
+                return fail(ZS3_EALIAS, "grads[%d] overlaps send", i);
+        }
+    }
+    if (do_reduce) {
+        if (recv_chunks == nullptr) return fail(ZS3_EINVAL, "recv_chunks is NULL");
+        if ((s = check_ptr16(grad_flat, "grad_flat")) != ZS3_OK) return s;
+        if ((s = check_partials(L, partials, grad_flat)) != ZS3_OK) return s;
+        for (int32_t v = 0; v < N; ++v) {
+            if ((s = check_ptr16(recv_chunks[v], "recv_chunks[v]")) != ZS3_OK) return s;
+            for (int32_t j = 0; j < n; ++j) {
+                const Slot& o = L->params[pos[j]];
+                if (overlap(recv_chunks[v], 2 * chunk, gbase + o.offset, 2 * o.ps))
+                    return fail(ZS3_EALIAS, "recv_chunks[%d] overlaps the written part of grad_flat", v);
+            }
+            if (partials != nullptr && overlap(recv_chunks[v], 2 * chunk, partials, 8 * L->n_slots))
+                return fail(ZS3_EALIAS, "recv_chunks[%d] overlaps partials", v);
+        }
+        if (do_pack)
+            for (int32_t j = 0; j < n; ++j) {
+                const Slot& o = L->params[pos[j]];
+                if (overlap(send, 2 * N * chunk, gbase + o.offset, 2 * o.ps))
+                    return fail(ZS3_EALIAS, "send overlaps the written part of grad_flat");
+            }
+    }
+    if (n == 0) return ok();
+
+    if (do_pack) {
+        Key key{{kOpScatterPack, device_id(), reinterpret_cast<int64_t>(send)}};
+        for (int32_t k : order) {
+            key.w.push_back(L->params[pos[k]].ds_id);
+            key.w.push_back(reinterpret_cast<int64_t>(grads[k]));
+        }
+        Plan* plan = find_plan(L, key);
+        if (plan == nullptr) {
+            // chunk d = partition d of every parameter in ascending ds_id, zeros past numel
+            std::vector<CopySeg> segs;
+            uint16_t* out = static_cast<uint16_t*>(send);
+            for (int32_t d = 0; d < N; ++d) {
+                for (int32_t k : order) {
+                    const Slot& p = L->params[pos[k]];
+                    int64_t lo, hi;
+                    p.own_range(d, &lo, &hi);
+                    uint16_t* dst = out + static_cast<int64_t>(d) * chunk + c[k];
+                    segs.push_back(CopySeg{static_cast<const uint16_t*>(grads[k]) + lo, dst, hi - lo, nullptr, 0});
+                    segs.push_back(CopySeg{nullptr, dst + (hi - lo), p.ps - (hi - lo), nullptr, 0});
+                }
+            }
+            if ((s = build_copy_plan(L, std::move(key), segs, &plan)) != ZS3_OK) return s;
+        }
+        if ((s = run_copy(kCopyScatterPack, plan, stream)) != ZS3_OK) return s;
+    }
+    if (do_reduce) {
+        Key key{{kOpScatterReduce, device_id(), rank, reinterpret_cast<int64_t>(grad_flat)}};
+        for (int32_t v = 0; v < N; ++v) key.w.push_back(reinterpret_cast<int64_t>(recv_chunks[v]));
+        for (int32_t k : order) key.w.push_back(L->params[pos[k]].ds_id);
+        Plan* plan = find_plan(L, key);
+        if (plan == nullptr) {
+            std::vector<RsSeg> segs;
+            std::vector<const uint16_t*> srcs;
+            for (int32_t k : order) {
+                const Slot& p = L->params[pos[k]];
+                const int64_t real = p.real(rank);
+                segs.push_back(RsSeg{gbase + p.offset, real, p.ps, static_cast<int64_t>(srcs.size()), L->slot_base[pos[k]]});
+                for (int32_t v = 0; v < N; ++v)
+                    srcs.push_back(real == 0 ? nullptr : static_cast<const uint16_t*>(recv_chunks[v]) + c[k]);
+            }
+            if ((s = build_rs_plan(L, std::move(key), segs, srcs, N, &plan)) != ZS3_OK) return s;
+        }
+        if ((s = run_rs(kRsCoalesced, plan, dtype, N, partials, stream)) != ZS3_OK) return s;
+    }
+    return ok();
 }
 
 // ---------------------------------------------------------------- (4)
@@ -850,6 +995,47 @@ zs3_status zs3_grad_norm(zs3_layout_t L, int32_t rank, int32_t dtype, const void
                                        sumsq, rank,
                                        L->world, finalize, max_norm, loss_scale, norm_out, scale_out, nonfinite,
                                        static_cast<hipStream_t>(stream)),
+                      "grad-norm kernel launch");
+}
+
+zs3_status zs3_layout_norm_slots(zs3_layout_t L, int64_t* n_slots, int64_t* n_part_slots) {
+    if (L == nullptr) return fail(ZS3_EINVAL, "layout is NULL");
+    if (n_slots) *n_slots = L->n_slots;
+    if (n_part_slots) *n_part_slots = L->n_part_slots;
+    return ok();
+}
+
+zs3_status zs3_grad_norm_partials(zs3_layout_t L, int32_t rank, const double* partials, double* sumsq,
+                                  int32_t finalize, double max_norm, double loss_scale, double* norm_out,
+                                  float* scale_out, int32_t* nonfinite, void* stream) {
+    zs3_status s = check_layout_rank(L, rank);
+    if (s != ZS3_OK) return s;
+    if (partials == nullptr || !aligned(partials, 8)) return fail(ZS3_EINVAL, "partials is NULL or not 8-byte aligned");
+    if (sumsq == nullptr || !aligned(sumsq, 8)) return fail(ZS3_EINVAL, "sumsq is NULL or not 8-byte aligned");
+    if (finalize) {
+        if (norm_out == nullptr || scale_out == nullptr || nonfinite == nullptr)
+            return fail(ZS3_EINVAL, "finalize needs norm_out, scale_out and nonfinite");
+        if (!aligned(norm_out, 8) || !aligned(scale_out, 4) || !aligned(nonfinite, 4))
+            return fail(ZS3_EINVAL, "misaligned norm_out, scale_out or nonfinite");
+        if (!(max_norm > 0.0) || !(loss_scale > 0.0)) return fail(ZS3_EINVAL, "max_norm and loss_scale must be > 0");
+    }
+    if (overlap(sumsq, 8 * (L->world + 1), partials, 8 * L->n_slots)) return fail(ZS3_EALIAS, "sumsq overlaps partials");
+    Key key{{kOpNormSlots, device_id()}};
+    Plan* plan = find_plan(L, key);
+    if (plan == nullptr) {
+        Plan np;
+        // about 1024 slots per workgroup, at most 1024 workgroups
+        np.n_blocks = std::max<int64_t>(1, std::min<int64_t>(1024, (L->n_slots + 1023) / 1024));
+        np.n_pieces = (L->n_slots + np.n_blocks - 1) / np.n_blocks;    // slots per workgroup
+        std::vector<size_t> offs;
+        s = upload(&np, {}, 2 * static_cast<size_t>(np.n_blocks) * sizeof(double), &offs);
+        if (s != ZS3_OK) return s;
+        store_plan(L, std::move(key), std::move(np), &plan);
+    }
+    return hip_status(launch_norm_from_slots(partials, L->n_slots, L->n_part_slots, plan->n_blocks, plan->n_pieces,
+                                             plan->at<double>(plan->off_scratch), sumsq, rank, L->world, finalize,
+                                             max_norm, loss_scale, norm_out, scale_out, nonfinite,
+                                             static_cast<hipStream_t>(stream)),
                       "grad-norm kernel launch");
 }
 

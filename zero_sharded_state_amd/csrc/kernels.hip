@@ -275,6 +275,36 @@ __global__ __launch_bounds__(kBlock) void k_copy_inline(const CopyInline plan) {
     copy_piece(plan.src[s], plan.dst[s], plan.dst2[s], plan.count2[s], begin, len, sub, threadIdx.x);
 }
 
+// ----------------------------------------------------- sums of squares
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// Deterministic workgroup sum: butterfly within each wave, then the four
+// wave totals in wave order.  Result valid in thread 0.
+__device__ __forceinline__ double block_sum(double x, double* sh) {
+    x = wave_sum(x);
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    if (lane == 0) sh[wv] = x;
+    __syncthreads();
+    double r = 0.0;
+    if (threadIdx.x == 0) {
+        for (int i = 0; i < kBlock / 64; ++i) r += sh[i];
+    }
+    __syncthreads();
+    return r;
+}
+
+template <int D>
+__device__ __forceinline__ double sq(uint32_t bits16) {
+    const double x = static_cast<double>(widen<D>(bits16));
+    return x * x;
+}
+
 // ---------------------------------------------------- reduce-scatter kernel
 // [codex] 6.2 / [csdn] step 3: own slice of the average of the N ranks'
 // gradients.  Each output element is ((0 + g_0) + g_1 + ... + g_{N-1}) / N
@@ -311,15 +341,26 @@ __device__ __forceinline__ uint16_t rs_elem(const SRC& sp, int world, Divider di
     return static_cast<uint16_t>(narrow<D>(div(acc)));
 }
 
-template <int D, bool ALIGNED, class SRC>
-__device__ __forceinline__ void rs_piece(const SRC& sp, uint16_t* seg_dst, int64_t real, int64_t begin,
-                                         int64_t len, int world, Divider div, int sub, int t) {
+// Writes one element and, with NORM, adds the square of what was written.
+template <int D, bool NORM, class SRC>
+__device__ __forceinline__ void rs_put(uint16_t* dst, const SRC& sp, int world, Divider div, int64_t k,
+                                       int64_t real, double& ss) {
+    const uint16_t x = rs_elem<D>(sp, world, div, k, real);
+    *dst = x;
+    if constexpr (NORM) ss += sq<D>(x);
+}
+
+// Returns the thread's sum of squares of the values it wrote (0 unless NORM).
+template <int D, bool ALIGNED, bool NORM, class SRC>
+__device__ __forceinline__ double rs_piece(const SRC& sp, uint16_t* seg_dst, int64_t real, int64_t begin,
+                                           int64_t len, int world, Divider div, int sub, int t) {
+    double ss = 0.0;
     int64_t k0 = begin;
     int64_t n = len;
     uint16_t* dst = seg_dst + k0;
     int64_t h = head16(dst);
     if (h > n) h = n;
-    if (sub == 0 && t < h) dst[t] = rs_elem<D>(sp, world, div, k0 + t, real);
+    if (sub == 0 && t < h) rs_put<D, NORM>(dst + t, sp, world, div, k0 + t, real, ss);
     k0 += h;
     dst += h;
     n -= h;
@@ -380,11 +421,13 @@ __device__ __forceinline__ void rs_piece(const SRC& sp, uint16_t* seg_dst, int64
         for (int u = 0; u < kRsVPT; ++u) {
             const int64_t i = i0 + t + int64_t(u) * kBlock;
             if (i < nfull) {
-                v4u o;
-                o.x = pack2(narrow<D>(div(acc[u][0])), narrow<D>(div(acc[u][1])));
-                o.y = pack2(narrow<D>(div(acc[u][2])), narrow<D>(div(acc[u][3])));
-                o.z = pack2(narrow<D>(div(acc[u][4])), narrow<D>(div(acc[u][5])));
-                o.w = pack2(narrow<D>(div(acc[u][6])), narrow<D>(div(acc[u][7])));
+                uint32_t b[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    b[e] = narrow<D>(div(acc[u][e]));
+                    if constexpr (NORM) ss += sq<D>(b[e]);
+                }
+                const v4u o = {pack2(b[0], b[1]), pack2(b[2], b[3]), pack2(b[4], b[5]), pack2(b[6], b[7])};
                 st_stream<kNtRs>(dst + 8 * i, o);
             }
         }
@@ -394,68 +437,107 @@ __device__ __forceinline__ void rs_piece(const SRC& sp, uint16_t* seg_dst, int64
     int64_t hi = i0 + int64_t(kBlock) * kRsVPT;
     if (hi > nv) hi = nv;
     for (int64_t i = lo + t; i < hi; i += kBlock) {
-        for (int e = 0; e < 8; ++e) dst[8 * i + e] = rs_elem<D>(sp, world, div, k0 + 8 * i + e, real);
+        for (int e = 0; e < 8; ++e) rs_put<D, NORM>(dst + 8 * i + e, sp, world, div, k0 + 8 * i + e, real, ss);
     }
     const int64_t rem = n & 7;
-    if (sub == kRsSub - 1 && t < rem) dst[nv * 8 + t] = rs_elem<D>(sp, world, div, k0 + nv * 8 + t, real);
+    if (sub == kRsSub - 1 && t < rem) rs_put<D, NORM>(dst + nv * 8 + t, sp, world, div, k0 + nv * 8 + t, real, ss);
+    return ss;
 }
 
-template <int D, bool ALIGNED>
-__global__ __launch_bounds__(kBlock) void k_reduce_scatter(const RsSeg* __restrict__ segs,
-                                                           const Piece* __restrict__ pieces,
-                                                           const uint16_t* const* __restrict__ srcs,
-                                                           int world, Divider div) {
+// Pieces of a slice of `total` elements whose destination needs `head`
+// elements to reach 16-byte alignment (the host's split), and the index of
+// the piece that starts at `begin`.
+__device__ __forceinline__ int64_t pieces_of(int64_t total, int64_t head) {
+    const int64_t first = total < head + kRsPiece ? total : head + kRsPiece;
+    return 1 + (total - first + kRsPiece - 1) / kRsPiece;
+}
+__device__ __forceinline__ int64_t piece_index(int64_t begin, int64_t head) {
+    return begin == 0 ? 0 : 1 + (begin - head - kRsPiece) / kRsPiece;
+}
+
+// The workgroup's partial sum goes to slot + q*kRsSub + sub; the last piece
+// of a slice that needs one piece fewer than the slot bound also zeroes the
+// spare group.
+__device__ __forceinline__ void put_partial(double ss, double* partials, int64_t slot, int64_t q, int64_t actual,
+                                            int64_t total, int sub, double* sh) {
+    const double s = block_sum(ss, sh);
+    if (threadIdx.x == 0) {
+        const int64_t at = slot + q * kRsSub + sub;
+        partials[at] = s;
+        if (q == actual - 1 && actual < norm_slot_groups(total)) partials[at + kRsSub] = 0.0;
+    }
+}
+
+template <int D, bool ALIGNED, bool NORM>
+__device__ __forceinline__ void rs_table(const RsSeg* __restrict__ segs, const Piece* __restrict__ pieces,
+                                         const uint16_t* const* __restrict__ srcs, int world, Divider div,
+                                         double* __restrict__ partials) {
+    __shared__ double sh[kBlock / 64];
     const uint32_t pidx = blockIdx.x / kRsSub;
     const int sub = static_cast<int>(blockIdx.x % kRsSub);
     const Piece pc = pieces[pidx];
     const RsSeg sg = segs[pc.seg];
     const TableSrcs sp{srcs + sg.src_index};
-    rs_piece<D, ALIGNED>(sp, sg.dst, sg.real, pc.begin, pc.len, world, div, sub, threadIdx.x);
+    const double ss = rs_piece<D, ALIGNED, NORM>(sp, sg.dst, sg.real, pc.begin, pc.len, world, div, sub, threadIdx.x);
+    if constexpr (NORM) {
+        const int64_t head = head16(sg.dst);
+        put_partial(ss, partials, sg.slot, piece_index(pc.begin, head), pieces_of(sg.total, head), sg.total, sub, sh);
+    }
 }
 
-template <int D, bool ALIGNED>
-__global__ __launch_bounds__(kBlock) void k_reduce_scatter_inline(const RsInline plan, Divider div) {
+template <int D, bool ALIGNED, bool NORM>
+__device__ __forceinline__ void rs_inline(const RsInline& plan, Divider div, double* __restrict__ partials) {
+    __shared__ double sh[kBlock / 64];
     const int32_t pidx = static_cast<int32_t>(blockIdx.x / kRsSub);
     const int sub = static_cast<int>(blockIdx.x % kRsSub);
     const int s = find_seg<kRsInlineSegs>(plan.piece_start, plan.nseg, pidx);
+    const int64_t q = pidx - plan.piece_start[s];
     int64_t begin, len;
-    piece_range(pidx - plan.piece_start[s], plan.total[s], plan.head[s], kRsPiece, &begin, &len);
+    piece_range(q, plan.total[s], plan.head[s], kRsPiece, &begin, &len);
     const InlineSrcs sp{plan, s * plan.world};
-    rs_piece<D, ALIGNED>(sp, plan.dst[s], plan.real[s], begin, len, plan.world, div, sub, threadIdx.x);
+    const double ss = rs_piece<D, ALIGNED, NORM>(sp, plan.dst[s], plan.real[s], begin, len, plan.world, div, sub,
+                                                 threadIdx.x);
+    if constexpr (NORM)
+        put_partial(ss, partials, plan.slot[s], q, plan.piece_start[s + 1] - plan.piece_start[s], plan.total[s], sub,
+                    sh);
+}
+
+// One body, two kernel names per form: the contiguous path (all-reduce of a
+// bucket, own interval kept) and the non-contiguous path's owner side
+// (reduce of the N received chunks); profiles attribute time to each.
+template <int D, bool ALIGNED, bool NORM>
+__global__ __launch_bounds__(kBlock) void k_reduce_scatter(const RsSeg* __restrict__ segs,
+                                                           const Piece* __restrict__ pieces,
+                                                           const uint16_t* const* __restrict__ srcs,
+                                                           int world, Divider div, double* __restrict__ partials) {
+    rs_table<D, ALIGNED, NORM>(segs, pieces, srcs, world, div, partials);
+}
+
+template <int D, bool ALIGNED, bool NORM>
+__global__ __launch_bounds__(kBlock) void k_reduce_scatter_inline(const RsInline plan, Divider div,
+                                                                  double* __restrict__ partials) {
+    rs_inline<D, ALIGNED, NORM>(plan, div, partials);
+}
+
+template <int D, bool ALIGNED, bool NORM>
+__global__ __launch_bounds__(kBlock) void k_scatter_reduce(const RsSeg* __restrict__ segs,
+                                                           const Piece* __restrict__ pieces,
+                                                           const uint16_t* const* __restrict__ srcs,
+                                                           int world, Divider div, double* __restrict__ partials) {
+    rs_table<D, ALIGNED, NORM>(segs, pieces, srcs, world, div, partials);
+}
+
+template <int D, bool ALIGNED, bool NORM>
+__global__ __launch_bounds__(kBlock) void k_scatter_reduce_inline(const RsInline plan, Divider div,
+                                                                  double* __restrict__ partials) {
+    rs_inline<D, ALIGNED, NORM>(plan, div, partials);
 }
 
 // ------------------------------------------------------------ grad norm
 // [llmnex] pitfall 1 / [codex] 6.3: local sums of squares, combined into one
 // global norm and one clip coefficient.  Squares are taken in double, where
-// the square of a 16-bit value is exact.
-
-__device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
-
-// Deterministic workgroup sum: butterfly within each wave, then the four
-// wave totals in wave order.  Result valid in thread 0.
-__device__ __forceinline__ double block_sum(double x, double* sh) {
-    x = wave_sum(x);
-    const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
-    if (lane == 0) sh[wv] = x;
-    __syncthreads();
-    double r = 0.0;
-    if (threadIdx.x == 0) {
-        for (int i = 0; i < kBlock / 64; ++i) r += sh[i];
-    }
-    __syncthreads();
-    return r;
-}
-
-template <int D>
-__device__ __forceinline__ double sq(uint32_t bits16) {
-    const double x = static_cast<double>(widen<D>(bits16));
-    return x * x;
-}
+// the square of a 16-bit value is exact (helpers above the reduce-scatter,
+// which can produce the same sums as it writes the averaged slice).
 
 // Grid-stride over (span, sub-block) work items; each workgroup keeps one
 // sum for partitioned spans [0, n_part) and one for persistent spans and
@@ -509,6 +591,30 @@ __global__ __launch_bounds__(kBlock) void k_sumsq(const uint16_t* __restrict__ g
     if (t == 0) {
         partials[2 * blockIdx.x] = a;
         partials[2 * blockIdx.x + 1] = b;
+    }
+}
+
+// Sum of the reduce-scatter's partial slots: workgroup b adds slots
+// [b*per_block, (b+1)*per_block) in a fixed order, partitioned ones (index
+// < n_part) and persistent ones apart.
+__global__ __launch_bounds__(kBlock) void k_sum_slots(const double* __restrict__ partials, int64_t n_slots,
+                                                      int64_t n_part, int64_t per_block,
+                                                      double* __restrict__ block_sums) {
+    __shared__ double sh[kBlock / 64];
+    const int64_t b0 = int64_t(blockIdx.x) * per_block;
+    int64_t b1 = b0 + per_block;
+    if (b1 > n_slots) b1 = n_slots;
+    double a = 0.0, b = 0.0;
+    for (int64_t i = b0 + threadIdx.x; i < b1; i += kBlock) {
+        const double x = partials[i];
+        if (i < n_part) a += x;
+        else b += x;
+    }
+    a = block_sum(a, sh);
+    b = block_sum(b, sh);
+    if (threadIdx.x == 0) {
+        block_sums[2 * blockIdx.x] = a;
+        block_sums[2 * blockIdx.x + 1] = b;
     }
 }
 
@@ -719,6 +825,7 @@ hipError_t launch_copy(CopyKind kind, const CopySeg* segs, const Piece* pieces, 
         case kCopyPartition: launch(k_copy<kCopyPartition>, g, b, stream, segs, pieces); break;
         case kCopyPack: launch(k_copy<kCopyPack>, g, b, stream, segs, pieces); break;
         case kCopyUnpack: launch(k_copy<kCopyUnpack>, g, b, stream, segs, pieces); break;
+        case kCopyScatterPack: launch(k_copy<kCopyScatterPack>, g, b, stream, segs, pieces); break;
         default: launch(k_copy<kCopyGather>, g, b, stream, segs, pieces); break;
     }
     return hipGetLastError();
@@ -732,6 +839,7 @@ hipError_t launch_copy_inline(CopyKind kind, const CopyInline& plan, hipStream_t
         case kCopyPartition: launch(k_copy_inline<kCopyPartition>, g, b, stream, plan); break;
         case kCopyPack: launch(k_copy_inline<kCopyPack>, g, b, stream, plan); break;
         case kCopyUnpack: launch(k_copy_inline<kCopyUnpack>, g, b, stream, plan); break;
+        case kCopyScatterPack: launch(k_copy_inline<kCopyScatterPack>, g, b, stream, plan); break;
         default: launch(k_copy_inline<kCopyGather>, g, b, stream, plan); break;
     }
     return hipGetLastError();
@@ -745,34 +853,85 @@ static Divider make_divider(int32_t world) {
     return div;
 }
 
-hipError_t launch_reduce_scatter(int32_t dtype, const RsSeg* segs, const Piece* pieces, int64_t n_pieces,
-                                 const uint16_t* const* srcs, int32_t world, bool co_aligned,
-                                 hipStream_t stream) {
+// The 16 forms of a reduce-scatter launch: path x dtype x co-alignment x
+// fused sums of squares.
+template <int D, bool A, bool NORM>
+void rs_launch_table(RsPath path, dim3 g, hipStream_t stream, const RsSeg* segs, const Piece* pieces,
+                     const uint16_t* const* srcs, int32_t world, Divider div, double* partials) {
+    if (path == kRsCoalesced)
+        launch((k_scatter_reduce<D, A, NORM>), g, dim3(kBlock), stream, segs, pieces, srcs, world, div, partials);
+    else
+        launch((k_reduce_scatter<D, A, NORM>), g, dim3(kBlock), stream, segs, pieces, srcs, world, div, partials);
+}
+
+template <int D, bool A, bool NORM>
+void rs_launch_inline(RsPath path, dim3 g, hipStream_t stream, const RsInline& plan, Divider div, double* partials) {
+    if (path == kRsCoalesced)
+        launch((k_scatter_reduce_inline<D, A, NORM>), g, dim3(kBlock), stream, plan, div, partials);
+    else
+        launch((k_reduce_scatter_inline<D, A, NORM>), g, dim3(kBlock), stream, plan, div, partials);
+}
+
+template <int D>
+void rs_dispatch_table(RsPath path, bool co, bool norm, dim3 g, hipStream_t stream, const RsSeg* segs,
+                       const Piece* pieces, const uint16_t* const* srcs, int32_t world, Divider div,
+                       double* partials) {
+    if (co) {
+        if (norm) rs_launch_table<D, true, true>(path, g, stream, segs, pieces, srcs, world, div, partials);
+        else rs_launch_table<D, true, false>(path, g, stream, segs, pieces, srcs, world, div, partials);
+    } else {
+        if (norm) rs_launch_table<D, false, true>(path, g, stream, segs, pieces, srcs, world, div, partials);
+        else rs_launch_table<D, false, false>(path, g, stream, segs, pieces, srcs, world, div, partials);
+    }
+}
+
+template <int D>
+void rs_dispatch_inline(RsPath path, bool co, bool norm, dim3 g, hipStream_t stream, const RsInline& plan,
+                        Divider div, double* partials) {
+    if (co) {
+        if (norm) rs_launch_inline<D, true, true>(path, g, stream, plan, div, partials);
+        else rs_launch_inline<D, true, false>(path, g, stream, plan, div, partials);
+    } else {
+        if (norm) rs_launch_inline<D, false, true>(path, g, stream, plan, div, partials);
+        else rs_launch_inline<D, false, false>(path, g, stream, plan, div, partials);
+    }
+}
+
+hipError_t launch_reduce_scatter(RsPath path, int32_t dtype, const RsSeg* segs, const Piece* pieces,
+                                 int64_t n_pieces, const uint16_t* const* srcs, int32_t world, bool co_aligned,
+                                 double* partials, hipStream_t stream) {
     if (n_pieces <= 0) return hipSuccess;
     const Divider div = make_divider(world);
-    const dim3 g = grid_of(n_pieces * kRsSub), b(kBlock);
-    if (dtype == kFP16) {
-        if (co_aligned) launch((k_reduce_scatter<kFP16, true>), g, b, stream, segs, pieces, srcs, world, div);
-        else launch((k_reduce_scatter<kFP16, false>), g, b, stream, segs, pieces, srcs, world, div);
-    } else {
-        if (co_aligned) launch((k_reduce_scatter<kBF16, true>), g, b, stream, segs, pieces, srcs, world, div);
-        else launch((k_reduce_scatter<kBF16, false>), g, b, stream, segs, pieces, srcs, world, div);
-    }
+    const dim3 g = grid_of(n_pieces * kRsSub);
+    const bool norm = partials != nullptr;
+    if (dtype == kFP16) rs_dispatch_table<kFP16>(path, co_aligned, norm, g, stream, segs, pieces, srcs, world, div, partials);
+    else rs_dispatch_table<kBF16>(path, co_aligned, norm, g, stream, segs, pieces, srcs, world, div, partials);
     return hipGetLastError();
 }
 
-hipError_t launch_reduce_scatter_inline(int32_t dtype, const RsInline& plan, bool co_aligned, hipStream_t stream) {
+hipError_t launch_reduce_scatter_inline(RsPath path, int32_t dtype, const RsInline& plan, bool co_aligned,
+                                        double* partials, hipStream_t stream) {
     const int64_t n_pieces = plan.piece_start[plan.nseg];
     if (n_pieces <= 0) return hipSuccess;
     const Divider div = make_divider(plan.world);
-    const dim3 g = grid_of(n_pieces * kRsSub), b(kBlock);
-    if (dtype == kFP16) {
-        if (co_aligned) launch((k_reduce_scatter_inline<kFP16, true>), g, b, stream, plan, div);
-        else launch((k_reduce_scatter_inline<kFP16, false>), g, b, stream, plan, div);
-    } else {
-        if (co_aligned) launch((k_reduce_scatter_inline<kBF16, true>), g, b, stream, plan, div);
-        else launch((k_reduce_scatter_inline<kBF16, false>), g, b, stream, plan, div);
+    const dim3 g = grid_of(n_pieces * kRsSub);
+    const bool norm = partials != nullptr;
+    if (dtype == kFP16) rs_dispatch_inline<kFP16>(path, co_aligned, norm, g, stream, plan, div, partials);
+    else rs_dispatch_inline<kBF16>(path, co_aligned, norm, g, stream, plan, div, partials);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_from_slots(const double* partials, int64_t n_slots, int64_t n_part, int64_t n_blocks,
+                                  int64_t per_block, double* block_sums, double* sumsq, int32_t rank,
+                                  int32_t world, int32_t finalize, double max_norm, double loss_scale,
+                                  double* norm_out, float* scale_out, int32_t* nonfinite, hipStream_t stream) {
+    if (n_blocks > 0) {
+        launch(k_sum_slots, grid_of(n_blocks), dim3(kBlock), stream, partials, n_slots, n_part, per_block, block_sums);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
+    launch(k_norm_finalize, dim3(1), dim3(kBlock), stream, static_cast<const double*>(block_sums), n_blocks, sumsq,
+           rank, world, finalize, max_norm, loss_scale, norm_out, scale_out, nonfinite);
     return hipGetLastError();
 }
 

@@ -97,13 +97,26 @@ struct Piece {
 };
 
 // Reduce-scatter of one parameter's own slice.  The N source pointers of
-// the segment are srcs[src_index .. src_index + N).
+// the segment are srcs[src_index .. src_index + N).  `slot` is the first of
+// the parameter's partial sum-of-squares slots (see norm_slot_groups).
 struct RsSeg {
     uint16_t* dst;
     int64_t real;        // averaged elements
     int64_t total;       // real + padding zeros (the partition size)
     int64_t src_index;
+    int64_t slot;
 };
+
+// Partial sums of squares written by the reduce-scatter kernels: every
+// parameter owns kRsSub * norm_slot_groups(partition_size) consecutive
+// slots, one per workgroup that can write its slice, at a position fixed by
+// the layout (partitioned parameters first, then persistent ones, each in
+// ascending ds_id), so buckets reduced in any order or on any stream write
+// disjoint slots.  A slice that needs one piece fewer than the bound zeroes
+// the spare group.
+__host__ __device__ constexpr int64_t norm_slot_groups(int64_t total) {
+    return total <= kRsPiece ? 1 : (total + kRsPiece - 1) / kRsPiece;
+}
 
 // Calls with few segments carry their whole plan in the kernel arguments
 // (structure of arrays, < 2 KB each): the workgroup finds its segment from
@@ -131,6 +144,7 @@ struct RsInline {
     uint16_t* dst[kRsInlineSegs];
     int64_t real[kRsInlineSegs];
     int64_t total[kRsInlineSegs];
+    int64_t slot[kRsInlineSegs];
     const uint16_t* src[kRsInlineSrcs];       // segment s, rank v at [s * world + v]
 };
 
@@ -161,7 +175,12 @@ enum DType : int32_t { kFP16 = 1, kBF16 = 2 };
 
 // kCopyGather: pack and unpack of one bucket in one launch (the unpack reads
 // the own rank's part from the shard, which is what the pack puts on the wire).
-enum CopyKind : int32_t { kCopyPartition = 1, kCopyPack = 2, kCopyUnpack = 3, kCopyGather = 4 };
+// kCopyScatterPack: the send side of the non-contiguous gradient path.
+enum CopyKind : int32_t { kCopyPartition = 1, kCopyPack = 2, kCopyUnpack = 3, kCopyGather = 4, kCopyScatterPack = 5 };
+
+// Which gradient path a reduce-scatter launch serves (kernel names differ so
+// that profiles tell them apart; the arithmetic is the same).
+enum RsPath : int32_t { kRsContiguous = 1, kRsCoalesced = 2 };
 
 // ---- launchers (kernels.hip) -------------------------------------------
 // The calling thread's next launch records its start/end into these events.
@@ -171,12 +190,21 @@ hipError_t launch_copy(CopyKind kind, const CopySeg* segs, const Piece* pieces, 
                        hipStream_t stream);
 
 hipError_t launch_copy_inline(CopyKind kind, const CopyInline& plan, hipStream_t stream);
-hipError_t launch_reduce_scatter_inline(int32_t dtype, const RsInline& plan, bool co_aligned,
-                                        hipStream_t stream);
+// partials: NULL, or the rank's slot array (fused sums of squares).
+hipError_t launch_reduce_scatter_inline(RsPath path, int32_t dtype, const RsInline& plan, bool co_aligned,
+                                        double* partials, hipStream_t stream);
 
-hipError_t launch_reduce_scatter(int32_t dtype, const RsSeg* segs, const Piece* pieces,
+hipError_t launch_reduce_scatter(RsPath path, int32_t dtype, const RsSeg* segs, const Piece* pieces,
                                  int64_t n_pieces, const uint16_t* const* srcs, int32_t world,
-                                 bool co_aligned, hipStream_t stream);
+                                 bool co_aligned, double* partials, hipStream_t stream);
+
+// Sums the slot array ([0, n_part) partitioned, the rest persistent) by
+// n_blocks workgroups of `per_block` slots each into block_sums[2*n_blocks],
+// then combines them as launch_grad_norm does.
+hipError_t launch_norm_from_slots(const double* partials, int64_t n_slots, int64_t n_part, int64_t n_blocks,
+                                  int64_t per_block, double* block_sums, double* sumsq, int32_t rank,
+                                  int32_t world, int32_t finalize, double max_norm, double loss_scale,
+                                  double* norm_out, float* scale_out, int32_t* nonfinite, hipStream_t stream);
 
 // Sums of squares of grad over the spans ([0, n_part) partitioned, the rest
 // persistent) by n_blocks workgroups into partials[2*n_blocks], then one

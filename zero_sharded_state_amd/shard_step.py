@@ -12,12 +12,19 @@ collectives, in the order the pages give ([llmnex] section 2, [codex]
 2. backward all-gather: the same again (parameters were released after the
    forward);
 3. reduce-scatter of every gradient bucket (backward order) into the flat
-   gradient buffer, from the slices the N ranks send to this rank;
+   gradient buffer.  Contiguous path ([codex] 6.2, the default): from the
+   slices the N ranks' all-reduced buckets hold for this rank.
+   Non-contiguous path (reduce_scatter_coalesced): the rank packs its own
+   full gradients into N rank-major chunks, and reduces the N chunks
+   addressed to it (its own plus N-1 stand-ins for what the peers send);
+   persistent gradients take the all-reduce path either way.  With
+   ``fuse_norm`` the reduce also writes the norm's partial sums of squares;
 4. the pre-step pass that puts every parameter back in partitioned form
    ([codex] 6.3): the own range of each gathered parameter is copied into
    the flat shard (it already holds those values, so the shard is
    unchanged);
-5. the global gradient norm and clip scale ([llmnex] pitfall 1);
+5. the global gradient norm and clip scale ([llmnex] pitfall 1), from
+   grad_flat or, with ``fuse_norm``, from the reduce's partial sums;
 6. fused Adam + cast per sub-group.
 
 No call synchronises; nothing is copied to the host.  All buffers are torch
@@ -46,8 +53,14 @@ class ShardStep:
     def __init__(self, *, world_size: int, rank: int, threshold: int, ds_ids: Sequence[int],
                  numels: Sequence[int], dtype: str, prefetch_bucket_size: int, reduce_bucket_size: int,
                  sub_group_size: int, adam: AdamConfig = AdamConfig(), max_norm: float = 1.0,
-                 device: str = "cuda", rs_streams: int = 1, gather_streams: int = 1):
+                 device: str = "cuda", rs_streams: int = 1, gather_streams: int = 1,
+                 fuse_norm: bool = False, reduce_path: str = "contiguous"):
         import torch
+
+        if reduce_path not in ("contiguous", "coalesced"):
+            raise ValueError(f"reduce_path {reduce_path!r} is not 'contiguous' or 'coalesced'")
+        self.fuse_norm = bool(fuse_norm)
+        self.reduce_path = reduce_path
 
         self.torch = torch
         self.N, self.rank, self.dtype = int(world_size), int(rank), dtype
@@ -104,6 +117,10 @@ class ShardStep:
         self.exp_avg = self.state[sa:sa + max(1, self.S)]
         self.exp_avg_sq = self.state[2 * sa:2 * sa + max(1, self.S)]
         self.sumsq = torch.zeros(self.N + 1, dtype=torch.float64, device=dev)
+        self.n_slots, _ = zs.zs3_layout_norm_slots(self.h)
+        self.partials = torch.zeros(max(1, self.n_slots), dtype=torch.float64, device=dev)
+        if reduce_path == "coalesced":
+            self._coalesced_buffers()
         self.outs = torch.zeros(2, dtype=torch.float64, device=dev)   # norm | scale (f32), flag (i32)
         self.t = 0
         # independent gradient buckets are spread over a few streams so that
@@ -131,6 +148,57 @@ class ShardStep:
         """Where virtual rank v's slice of parameter ds_id for this rank lives."""
         return self.recv.data_ptr() + 2 * (v * self.S + self.by_id[ds_id]["shard_offset"])
 
+    def _coalesced_buffers(self):
+        """Own full gradients, per-bucket send buffers and received chunks.
+        Every chunk the reduce reads starts at the byte address of its
+        bucket's first grad_flat position modulo 16, so the reduce runs
+        co-aligned."""
+        torch = self.torch
+        part = [p for p in self.params if not p["persistent"]]
+        self.grad_off: Dict[int, int] = {}
+        o = 0
+        for p in part:
+            self.grad_off[p["ds_id"]] = o
+            o = (o + p["numel"] + 7) // 8 * 8
+        self.own_grads = torch.zeros(max(1, o), dtype=torch.int16, device=self.device)
+        gp = self.grad.data_ptr()
+        buckets = []          # (ids_part, ids_pers, C, send_off, {v: chunk_off})
+        cursor = 0
+
+        def place(n, residue):              # element offset with (2*off) % 16 == residue
+            nonlocal cursor
+            off = cursor + ((residue // 2 - cursor) % 8)
+            cursor = off + n
+            return off
+
+        for b in self.reduce_buckets:
+            ids_part = sorted(d for d in b if not self.by_id[d]["persistent"])
+            ids_pers = [d for d in b if self.by_id[d]["persistent"]]
+            C = sum(self.by_id[d]["partition_size"] for d in ids_part)
+            if not ids_part:
+                buckets.append((ids_part, ids_pers, 0, 0, {}))
+                continue
+            res = (gp + 2 * self.by_id[ids_part[0]]["shard_offset"]) % 16
+            send = place(self.N * C, (res - 2 * self.rank * C) % 16)
+            chunks = {v: place(C, res) for v in range(self.N) if v != self.rank}
+            buckets.append((ids_part, ids_pers, C, send, chunks))
+        self.xbuf = torch.zeros(max(1, cursor), dtype=torch.int16, device=self.device)
+        self.coalesced = buckets
+
+    def grad_ptr(self, ds_id: int) -> int:
+        """This rank's full gradient of a partitioned parameter (non-contiguous path)."""
+        return self.own_grads.data_ptr() + 2 * self.grad_off[ds_id]
+
+    def recv_chunk_ptr(self, bucket: int, v: int) -> int:
+        """The chunk virtual rank v sends to this rank for a gradient bucket."""
+        _, _, C, send, chunks = self.coalesced[bucket]
+        if v == self.rank:
+            return self.xbuf.data_ptr() + 2 * (send + v * C)
+        return self.xbuf.data_ptr() + 2 * chunks[v]
+
+    def send_ptr(self, bucket: int) -> int:
+        return self.xbuf.data_ptr() + 2 * self.coalesced[bucket][3]
+
     @property
     def norm_ptr(self) -> int:
         return self.outs.data_ptr()
@@ -155,7 +223,18 @@ class ShardStep:
             self._g.append((len(b), ids, self.chunk_ptr(bi, self.rank), chunks,
                             self.full.data_ptr() + 2 * fo))
         self._r = []
-        for b in self.reduce_buckets:
+        self._x = []
+        for bi, b in enumerate(self.reduce_buckets):
+            if self.reduce_path == "coalesced":
+                ids_part, ids_pers, C, _, _ = self.coalesced[bi]
+                b = ids_pers
+                if ids_part:
+                    self._x.append((len(ids_part), (I64 * len(ids_part))(*ids_part),
+                                    (P * len(ids_part))(*[self.grad_ptr(d) for d in ids_part]),
+                                    self.send_ptr(bi),
+                                    (P * self.N)(*[self.recv_chunk_ptr(bi, v) for v in range(self.N)])))
+                if not b:
+                    continue
             ids = (I64 * len(b))(*b)
             src = (P * (len(b) * self.N))(*[self.recv_ptr(v, d) for d in b for v in range(self.N)])
             self._r.append((len(b), ids, src))
@@ -224,9 +303,14 @@ class ShardStep:
         streams and joined back into the main stream."""
         main, aux, handles = self._fanout(stream, self.rs_streams)
         lib = zs.lib()
-        for i, (n, ids, src) in enumerate(self._r):
+        partials = self.partials.data_ptr() if self.fuse_norm else None
+        for i, (n, ids, grads, send, recv) in enumerate(self._x):
+            self._ok(lib.zs3_reduce_scatter_coalesced(self.h, self.rank, self.dcode, zs.ZS3_PACK | zs.ZS3_REDUCE,
+                                                      n, ids, grads, send, recv, self.grad.data_ptr(), partials,
+                                                      handles[i % len(handles)]))
+        for i, (n, ids, src) in enumerate(self._r, start=len(self._x)):
             self._ok(lib.zs3_reduce_scatter_local(self.h, self.rank, self.dcode, n, ids, src,
-                                                  self.grad.data_ptr(), handles[i % len(handles)]))
+                                                  self.grad.data_ptr(), partials, handles[i % len(handles)]))
         self._join(main, aux)
 
     def repartition(self, stream=None):
@@ -235,6 +319,12 @@ class ShardStep:
                                         stream if stream is not None else self._stream()))
 
     def grad_norm(self, finalize: bool = True, stream=None):
+        if self.fuse_norm:
+            self._ok(zs.lib().zs3_grad_norm_partials(self.h, self.rank, self.partials.data_ptr(),
+                                                     self.sumsq.data_ptr(), int(finalize), self.max_norm, 1.0,
+                                                     self.norm_ptr, self.scale_ptr, self.flag_ptr,
+                                                     stream if stream is not None else self._stream()))
+            return
         self._ok(zs.lib().zs3_grad_norm(self.h, self.rank, self.dcode, self.grad.data_ptr(), self.sumsq.data_ptr(),
                                         int(finalize), self.max_norm, 1.0, self.norm_ptr, self.scale_ptr,
                                         self.flag_ptr, stream if stream is not None else self._stream()))
@@ -303,14 +393,31 @@ class ShardStep:
         part_real = sum(p["own"][1] - p["own"][0] for p in self.params if not p["persistent"])
         own = self.own_real
         F = self.F
-        return {
+        out = {
             "pack": 2 * 4 * part_real,          # two passes, read + write of the real own shard elements
             "unpack": 2 * 4 * F,                # two passes, read N pieces + write the full parameters
             "reduce_scatter": 2 * N * own + 2 * own,
             "partition": 4 * own,
-            "grad_norm": 2 * own,
+            "grad_norm": 0 if self.fuse_norm else 2 * own,    # fused: no second read of grad_flat
             "adam": 28 * own,
         }
+        if self.reduce_path == "coalesced":
+            # send side: read the own full gradients, write N chunks (padding zeros included)
+            full_part = sum(p["numel"] for p in self.params if not p["persistent"])
+            chunks = sum(C for _, _, C, _, _ in self.coalesced)
+            out["scatter_pack"] = 2 * full_part + 2 * N * chunks
+        return out
+
+    def budget_bytes(self) -> int:
+        """The step's fixed algorithmic byte budget: forward and backward
+        gather (pack + unpack), the reduce-scatter, the re-partition, a norm
+        that reads the flat gradient once, and Adam -- the same work for every
+        variant of the step, so that effective bandwidth compares them at
+        equal work."""
+        N = self.N
+        part_real = sum(p["own"][1] - p["own"][0] for p in self.params if not p["persistent"])
+        own = self.own_real
+        return 2 * 4 * part_real + 2 * 4 * self.F + (2 * N + 2) * own + 4 * own + 2 * own + 28 * own
 
     def destroy(self):
         if self.h:
