@@ -50,10 +50,10 @@ def parse():
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=12, help="decoder layers in the oracle's sample")
-    ap.add_argument("--rs-streams", type=int, default=1, help="streams the gradient buckets are spread over")
+    ap.add_argument("--rs-streams", type=int, default=3, help="streams the gradient buckets are spread over")
     ap.add_argument("--gather-streams", type=int, default=1, help="streams the gather buckets are spread over")
     ap.add_argument("--no-kernel-timer", action="store_true", help="do not time the gather launches")
-    ap.add_argument("--fuse-norm", type=int, default=0, choices=(0, 1),
+    ap.add_argument("--fuse-norm", type=int, default=1, choices=(0, 1),
                     help="1: the reduce-scatter also writes the norm's partial sums (no second read of grad_flat)")
     ap.add_argument("--reduce-path", default="contiguous", choices=("contiguous", "coalesced"),
                     help="gradient path: all-reduced buckets (default) or reduce_scatter_coalesced")
@@ -383,7 +383,8 @@ def main():
             "gather_buckets": len(step.gather_buckets), "reduce_buckets": len(step.reduce_buckets),
             "sub_groups": len(step.sub_groups), "prefetch_bucket_size": cfg.prefetch_bucket_size,
             "reduce_bucket_size": cfg.reduce_bucket_size, "sub_group_size": cfg.sub_group_size,
-            "reduce_path": step.reduce_path, "fused_norm": step.fuse_norm,
+            "reduce_path": step.reduce_path, "fused_norm": step.fuse_norm, "rs_streams": step.rs_streams,
+            "gather_streams": step.gather_streams,
         },
         "kernels": kernels,
         "roofline": roofline,

@@ -186,14 +186,15 @@ def test_call_validation_enqueues_nothing():
         zs.zs3_layout_destroy(h)
 
 
-def _slot_count(ps_list, piece=256 * 8 * 8, sub=8):
-    return sum(sub * (1 if ps <= piece else -(-ps // piece)) for ps in ps_list)
+def _slot_count(ps_list, piece=256 * 8 * 8, per_piece=8 * 4):
+    return sum(per_piece * (1 if ps <= piece else -(-ps // piece)) for ps in ps_list)
 
 
 @pytest.mark.parametrize("name", sorted(CONFIGS))
 def test_norm_slots_cover_every_parameter(name):
-    """One group of workgroup slots per reduce-scatter piece of each
-    parameter's partition, partitioned parameters first."""
+    """One group of slots (one per wave of the piece's workgroups) per
+    reduce-scatter piece of each parameter's partition, partitioned
+    parameters first."""
     cfg = get_config(name)
     h, ol = _both(name)
     try:

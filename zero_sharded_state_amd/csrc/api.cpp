@@ -493,7 +493,7 @@ zs3_status zs3_layout_create(int32_t world_size, int64_t persistence_threshold, 
             const Slot& p = L->params[k];
             if (p.persistent != (pass == 1)) continue;
             L->slot_base[k] = slot;
-            slot += kRsSub * norm_slot_groups(p.ps);
+            slot += kNormSlotsPerGroup * norm_slot_groups(p.ps);
         }
         if (pass == 0) L->n_part_slots = slot;
     }

@@ -305,6 +305,24 @@ __device__ __forceinline__ double sq(uint32_t bits16) {
     return x * x;
 }
 
+// The same exact square with one fp64 operation fewer: the square of an
+// fp16 value (11-bit significand, |x| <= 65504, |x| >= 2^-24) is exact in
+// fp32, and so is that of a bf16 value whose biased exponent lies in
+// [64, 190] (8-bit significand, square a normal fp32); other bf16 values
+// (zero, tiny, huge, inf, NaN) take the fp64 square.
+template <int D>
+__device__ __forceinline__ double sq_fast(uint32_t bits16) {
+    const float x = widen<D>(bits16);
+    if constexpr (D == kFP16) {
+        return static_cast<double>(x * x);
+    } else {
+        const uint32_t e = (bits16 >> 7) & 0xffu;
+        if (e - 64u <= 126u) return static_cast<double>(x * x);
+        const double xd = static_cast<double>(x);
+        return xd * xd;
+    }
+}
+
 // ---------------------------------------------------- reduce-scatter kernel
 // [codex] 6.2 / [csdn] step 3: own slice of the average of the N ranks'
 // gradients.  Each output element is ((0 + g_0) + g_1 + ... + g_{N-1}) / N
@@ -347,7 +365,7 @@ __device__ __forceinline__ void rs_put(uint16_t* dst, const SRC& sp, int world, 
                                        int64_t real, double& ss) {
     const uint16_t x = rs_elem<D>(sp, world, div, k, real);
     *dst = x;
-    if constexpr (NORM) ss += sq<D>(x);
+    if constexpr (NORM) ss += sq_fast<D>(x);
 }
 
 // Returns the thread's sum of squares of the values it wrote (0 unless NORM).
@@ -425,7 +443,7 @@ __device__ __forceinline__ double rs_piece(const SRC& sp, uint16_t* seg_dst, int
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     b[e] = narrow<D>(div(acc[u][e]));
-                    if constexpr (NORM) ss += sq<D>(b[e]);
+                    if constexpr (NORM) ss += sq_fast<D>(b[e]);
                 }
                 const v4u o = {pack2(b[0], b[1]), pack2(b[2], b[3]), pack2(b[4], b[5]), pack2(b[6], b[7])};
                 st_stream<kNtRs>(dst + 8 * i, o);
@@ -460,11 +478,22 @@ __device__ __forceinline__ int64_t piece_index(int64_t begin, int64_t head) {
 // spare group.
 __device__ __forceinline__ void put_partial(double ss, double* partials, int64_t slot, int64_t q, int64_t actual,
                                             int64_t total, int sub, double* sh) {
-    const double s = block_sum(ss, sh);
-    if (threadIdx.x == 0) {
-        const int64_t at = slot + q * kRsSub + sub;
-        partials[at] = s;
-        if (q == actual - 1 && actual < norm_slot_groups(total)) partials[at + kRsSub] = 0.0;
+    const bool spare = q == actual - 1 && actual < norm_slot_groups(total);
+    if constexpr (kSlotsPerWG == 1) {
+        const double s = block_sum(ss, sh);
+        if (threadIdx.x == 0) {
+            const int64_t at = slot + q * kRsSub + sub;
+            partials[at] = s;
+            if (spare) partials[at + kRsSub] = 0.0;
+        }
+    } else {
+        // one slot per wave: no barrier, each wave's lane 0 writes its sum
+        const double s = wave_sum(ss);
+        if ((threadIdx.x & 63) == 0) {
+            const int64_t at = slot + (q * kRsSub + sub) * kSlotsPerWG + (threadIdx.x >> 6);
+            partials[at] = s;
+            if (spare) partials[at + kNormSlotsPerGroup] = 0.0;
+        }
     }
 }
 

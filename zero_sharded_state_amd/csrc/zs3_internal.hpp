@@ -108,12 +108,18 @@ struct RsSeg {
 };
 
 // Partial sums of squares written by the reduce-scatter kernels: every
-// parameter owns kRsSub * norm_slot_groups(partition_size) consecutive
-// slots, one per workgroup that can write its slice, at a position fixed by
+// parameter owns kNormSlotsPerGroup * norm_slot_groups(partition_size)
+// consecutive slots, kSlotsPerWG per workgroup that can write its slice
+// (one per workgroup, or one per wave), at a position fixed by
 // the layout (partitioned parameters first, then persistent ones, each in
 // ascending ds_id), so buckets reduced in any order or on any stream write
 // disjoint slots.  A slice that needs one piece fewer than the bound zeroes
 // the spare group.
+#ifndef ZS3_NORM_WAVE_SLOTS
+#define ZS3_NORM_WAVE_SLOTS 1
+#endif
+constexpr int kSlotsPerWG = ZS3_NORM_WAVE_SLOTS ? kBlock / 64 : 1;
+constexpr int64_t kNormSlotsPerGroup = int64_t(kRsSub) * kSlotsPerWG;
 __host__ __device__ constexpr int64_t norm_slot_groups(int64_t total) {
     return total <= kRsPiece ? 1 : (total + kRsPiece - 1) / kRsPiece;
 }
