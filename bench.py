@@ -57,6 +57,9 @@ def parse():
                     help="1: the reduce-scatter also writes the norm's partial sums (no second read of grad_flat)")
     ap.add_argument("--reduce-path", default="contiguous", choices=("contiguous", "coalesced"),
                     help="gradient path: all-reduced buckets (default) or reduce_scatter_coalesced")
+    ap.add_argument("--schedule", default="static", choices=("static", "trace"),
+                    help="parameter gathers: static gather buckets twice (default), or the buckets the "
+                         "trace-driven fetch/release coordinator returns over the forward+backward module order")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -243,6 +246,60 @@ def cpu_baseline(step, cfg, layers: int):
     }
 
 
+def coordinator_cost(step, cfg, steps: int = 5):
+    """Host cost of the fetch/release coordinator on the workload's module
+    order: the library's (through ctypes, preallocated arguments) and the
+    oracle's, per fetch or release call, on a complete trace."""
+    import ctypes
+
+    import zero_sharded_state_amd as zs
+    from oracle import coordinator as co
+    from synth.modules import module_table, step_order
+
+    _, mods = module_table(cfg)
+    order = step_order(cfg)
+    cc = co.CoordConfig(cfg.prefetch_bucket_size, int(1e9), int(1e9))
+    c = zs.zs3_coord_create(step.h, mods, cc.__dict__)
+    lib = zs.lib()
+    cap = sum(len(m) for m in mods)
+    ids = (ctypes.c_int64 * cap)()
+    kinds, starts, n = (ctypes.c_int32 * 2)(), (ctypes.c_int32 * 3)(), ctypes.c_int32()
+
+    def native_step():
+        for m in order:
+            lib.zs3_coord_fetch(c, m, ctypes.byref(n), kinds, starts, ids)
+            lib.zs3_coord_release(c, m, ctypes.byref(n), ids)
+        lib.zs3_coord_release_all(c, ctypes.byref(n), ids)
+        lib.zs3_coord_reset_step(c, None)
+
+    for _ in range(2):
+        native_step()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        native_step()
+    native = (time.perf_counter() - t0) / (steps * 2 * len(order)) * 1e6
+    zs.zs3_coord_destroy(c)
+
+    o = co.Coordinator({d: p.numel for d, p in enumerate(cfg.params)},
+                       {d: p.numel < cfg.threshold for d, p in enumerate(cfg.params)}, mods, cc)
+
+    def oracle_step():
+        for m in order:
+            o.fetch(m)
+            o.release(m)
+        o.release_all()
+        o.reset_step()
+
+    for _ in range(2):
+        oracle_step()
+    t0 = time.perf_counter()
+    oracle_step()
+    orc = (time.perf_counter() - t0) / (2 * len(order)) * 1e6
+    return {"calls_per_step": 2 * len(order), "us_per_call_library": round(native, 2),
+            "us_per_call_oracle": round(orc, 2),
+            "note": "library timed through ctypes with preallocated arguments (includes the call overhead)"}
+
+
 # --------------------------------------------------------------------------
 
 def main():
@@ -269,8 +326,23 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs resident in HBM ({torch.cuda.memory_allocated() / 2**30:.1f} GiB) in {time.time() - t0:.1f} s")
 
+    trace = None
+    if args.schedule == "trace":
+        from synth.modules import module_table, step_order
+        from zero_sharded_state_amd.trace_schedule import TraceGatherPass
+        _, mods = module_table(cfg)
+        trace = TraceGatherPass(step, mods, step_order(cfg),
+                                {"prefetch_bucket_size": cfg.prefetch_bucket_size,
+                                 "max_live_parameters": int(1e9), "max_reuse_distance": int(1e9)})
+        t1 = time.time()
+        trace.plan()
+        trace.fill_peer_chunks()
+        torch.cuda.synchronize()
+        log(f"coordinator: {len(trace.ops)} gathers per step ({trace.kinds.count(1)} prefetch), "
+            f"{trace.gathered:,} elements gathered, set up in {time.time() - t1:.1f} s")
+
     for _ in range(args.warmup):
-        step.step()
+        step.step(trace_pass=trace)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
@@ -293,13 +365,16 @@ def main():
     t_start = time.perf_counter()
     for _ in range(args.steps):
         phase_events.append([])
-        step.step(on_phase=on_phase, gather_timer=timer if per_launch else None)
+        step.step(on_phase=on_phase, gather_timer=timer if per_launch else None, trace_pass=trace)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     log(f"timed {args.steps} steps in {wall:.3f} s")
 
     ms_per_step = wall * 1e3 / args.steps
     nbytes = step.algorithmic_bytes()          # what this variant of the step must move, per kernel
+    if trace is not None:
+        del nbytes["pack"], nbytes["unpack"]
+        nbytes["gather_trace"] = trace.algorithmic_bytes()
     total_bytes = step.budget_bytes()          # the step's fixed budget (equal work for every variant)
     moved_bytes = sum(nbytes.values())
     gbs = total_bytes / (ms_per_step * 1e-3) / 1e9
@@ -310,8 +385,9 @@ def main():
     for evs in phase_events:
         for (name, e0), (_, e1) in zip(evs, evs[1:]):
             phases[name] = phases.get(name, 0.0) + e0.elapsed_time(e1)
-    phase_bytes = {"gather_fwd": (nbytes["pack"] + nbytes["unpack"]) // 2,
-                   "gather_bwd": (nbytes["pack"] + nbytes["unpack"]) // 2,
+    phase_bytes = {"gather_fwd": (nbytes.get("pack", 0) + nbytes.get("unpack", 0)) // 2,
+                   "gather_bwd": (nbytes.get("pack", 0) + nbytes.get("unpack", 0)) // 2,
+                   "gather_trace": nbytes.get("gather_trace", 0),
                    "reduce_scatter": nbytes["reduce_scatter"] + nbytes.get("scatter_pack", 0),
                    "partition": nbytes["partition"],
                    "grad_norm": nbytes["grad_norm"], "adam": nbytes["adam"]}
@@ -326,19 +402,20 @@ def main():
 
     # Roofline entry of the dominant kernel: the fused gather (pack + unpack
     # of one bucket, k_copy<4>), average duration over the timed launches.
-    launches = 2 * len(step.gather_buckets) * args.steps
+    launches = (len(trace.ops) if trace is not None else 2 * len(step.gather_buckets)) * args.steps
     if per_launch:
         durs = timer.durations_ms()
         avg_ms = sum(durs) / len(durs)
     else:
-        avg_ms = sum(phases.get(k, 0.0) for k in ("gather_fwd", "gather_bwd")) / launches
+        avg_ms = sum(phases.get(k, 0.0) for k in ("gather_fwd", "gather_bwd", "gather_trace")) / launches
     timer.close()
-    gather_bytes = nbytes["pack"] + nbytes["unpack"]
-    per_launch_bytes = gather_bytes / (2 * len(step.gather_buckets))
+    gather_bytes = nbytes["gather_trace"] if trace is not None else nbytes["pack"] + nbytes["unpack"]
+    per_launch_bytes = gather_bytes * args.steps / launches
     achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
     roofline = {"kernel": "gather: pack + unpack of one bucket (k_copy_inline<4>)", "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_entry(cfg.name),
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_entry(cfg.name) if trace is None else None,
                 "launches": launches, "avg_launch_ms": round(avg_ms, 5),
                 "algorithmic_bytes_per_launch": int(per_launch_bytes),
                 "streams": step.gather_streams}
@@ -351,6 +428,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+
+    coord = None
+    if trace is not None:
+        coord = coordinator_cost(step, cfg)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -384,11 +465,13 @@ def main():
             "sub_groups": len(step.sub_groups), "prefetch_bucket_size": cfg.prefetch_bucket_size,
             "reduce_bucket_size": cfg.reduce_bucket_size, "sub_group_size": cfg.sub_group_size,
             "reduce_path": step.reduce_path, "fused_norm": step.fuse_norm, "rs_streams": step.rs_streams,
+            "schedule": args.schedule,
             "gather_streams": step.gather_streams,
         },
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "coordinator": coord,
         "source_digest": source_digest(),
     }
     print(json.dumps(line), flush=True)

@@ -363,6 +363,85 @@ ZS3_API zs3_status zs3_adam_step(zs3_layout_t layout, int32_t rank, int32_t dtyp
                          void* shard_flat, const float* scale, const int32_t* nonfinite,
                          const zs3_adam_params* hp, void* stream);
 
+/* ------------------------------------ (f2) trace-driven fetch/release plan
+ * [codex] 5: a coordinator decides, module by module, which parameters to
+ * all-gather and when to put them back in partitioned form.  Host only: no
+ * device work; the gathers it returns are buckets for zs3_gather_coalesced.
+ *
+ * 5.1 trace.  Mode INVALID -> RECORD -> COMPLETE, advanced by
+ * zs3_coord_reset_step at each end of step: the first step runs without a
+ * trace, the second records the module order, and from the third on the
+ * recorded order (as a parameter-level script) drives prefetching.  A fetch
+ * that differs from the script drops the trace for the rest of the step
+ * (mode INVALID, prefetching stops) and the next steps record it again
+ * ([codex] section 7: dynamic graphs defeat prefetching).  A step that ends
+ * with fewer or more fetches than the script counts as a mismatch too.
+ * 5.2 fetch.  (i) The module's partitioned parameters that are not live are
+ * gathered now (kind ZS3_GATHER_CURRENT); (ii) the caller waits for the
+ * module's gathers; (iii) with a complete trace, the parameters that follow
+ * in the script and are not live are popped into one more gather (kind
+ * ZS3_GATHER_PREFETCH) until it holds prefetch_bucket_size elements (an
+ * oversize parameter fills a bucket alone) or the next one would take the
+ * live total past max_live_parameters; live parameters met on the way are
+ * marked as needed at that later use.
+ * 5.3 release.  A module's parameters go back to partitioned form unless the
+ * prefetcher marked a later use, or (complete trace) a module within
+ * max_reuse_distance elements further on uses them (the distance of a later
+ * module = elements of the partitioned parameters of the modules strictly
+ * between).  Persistent parameters are never gathered or released.
+ * Readings: a parameter is live (counted against max_live_parameters) from
+ * the issue of its gather to its release; every list is in ascending ds_id.
+ */
+typedef struct zs3_coord* zs3_coord_t;
+
+typedef struct {
+    int64_t prefetch_bucket_size;   /* elements per prefetch gather; 0 disables prefetching */
+    int64_t max_live_parameters;    /* elements of gathered parameters that prefetching may not pass */
+    int64_t max_reuse_distance;     /* elements */
+} zs3_coord_config;
+
+enum { ZS3_TRACE_INVALID = 0, ZS3_TRACE_RECORD = 1, ZS3_TRACE_COMPLETE = 2 };
+enum { ZS3_PARAM_NOT_AVAILABLE = 0, ZS3_PARAM_INFLIGHT = 1, ZS3_PARAM_AVAILABLE = 2 };
+enum { ZS3_GATHER_CURRENT = 0, ZS3_GATHER_PREFETCH = 1 };
+
+/* Module m owns module_ds_ids[module_start[m] .. module_start[m+1]) (host;
+ * module_start has n_modules+1 ascending entries from 0; ds_ids unique
+ * within a module and in the layout; a parameter may belong to several
+ * modules, e.g. tied weights).  The layout is read during the call only. */
+ZS3_API zs3_status zs3_coord_create(zs3_layout_t layout, int32_t n_modules, const int32_t* module_start,
+                            const int64_t* module_ds_ids, const zs3_coord_config* cfg, zs3_coord_t* out);
+ZS3_API void zs3_coord_destroy(zs3_coord_t coord);
+
+/* Fetch module m (before its forward or backward computation).  Outputs
+ * (host): *n_gathers (0, 1 or 2) gathers, gather g being
+ * ds_ids[starts[g] .. starts[g+1]) of kind kinds[g]; kinds needs 2 entries,
+ * starts 3, ds_ids room for every parameter of the modules. */
+ZS3_API zs3_status zs3_coord_fetch(zs3_coord_t coord, int32_t module, int32_t* n_gathers, int32_t* kinds,
+                           int32_t* starts, int64_t* ds_ids);
+/* Release module m (after its computation); m must have been fetched in
+ * this step and not released since.  *n_released ds_ids (host) go back to
+ * partitioned form. */
+ZS3_API zs3_status zs3_coord_release(zs3_coord_t coord, int32_t module, int32_t* n_released, int64_t* ds_ids);
+/* The pre-step pass ([codex] 6.3): every gathered parameter goes back to
+ * partitioned form. */
+ZS3_API zs3_status zs3_coord_release_all(zs3_coord_t coord, int32_t* n_released, int64_t* ds_ids);
+/* End of step: the trace-mode transition of 5.1; *mode (may be NULL)
+ * receives the new mode. */
+ZS3_API zs3_status zs3_coord_reset_step(zs3_coord_t coord, int32_t* mode);
+/* Current mode, live elements, recorded fetches, trace drops so far (any
+ * output may be NULL). */
+ZS3_API zs3_status zs3_coord_info(zs3_coord_t coord, int32_t* mode, int64_t* live_numel, int32_t* trace_len,
+                          int32_t* invalidations);
+ZS3_API zs3_status zs3_coord_param_status(zs3_coord_t coord, int64_t ds_id, int32_t* status);
+/* What ranks must agree on once a trace is recorded ([codex] 5.1: module
+ * order, parameter order, number of fetches): 64-bit FNV-1a over the
+ * little-endian int64 module ids of the trace and over the ds_ids of the
+ * parameter-level script, and the trace length.  Ranks compare them (for
+ * example by an all-reduce of min and max); a difference would make their
+ * collectives disagree. */
+ZS3_API zs3_status zs3_coord_trace_signature(zs3_coord_t coord, uint64_t* module_order, uint64_t* param_order,
+                                     int32_t* n_fetches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,6 +28,8 @@ Modules:
   pack and owner-side reduce), shard-aware grad norm, fused Adam + cast.
 * ``brute``  -- pure-Python per-element loops for tiny inputs, used only to
   pin ``zero3`` (a second, differently structured derivation).
+* ``coordinator`` -- the trace-driven fetch/release coordinator as a
+  step-by-step simulation (imported as ``oracle.coordinator``).
 
 Parity status of each function is stated in its docstring; the only
 function without an independent pin is the decoupled weight-decay branch of

@@ -28,7 +28,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     syms = _declared_symbols()
-    assert len(syms) == 21
+    assert len(syms) == 30
     assert sorted(zs.EXPORTS) == syms
     for s in syms:
         assert hasattr(L, s), s

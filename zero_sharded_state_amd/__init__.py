@@ -34,6 +34,9 @@ ZS3_UNPACK = 2
 ZS3_REDUCE = 4
 ZS3_GATHER_BUCKETS = 1
 ZS3_REDUCE_BUCKETS = 2
+ZS3_TRACE_INVALID, ZS3_TRACE_RECORD, ZS3_TRACE_COMPLETE = 0, 1, 2
+ZS3_PARAM_NOT_AVAILABLE, ZS3_PARAM_INFLIGHT, ZS3_PARAM_AVAILABLE = 0, 1, 2
+ZS3_GATHER_CURRENT, ZS3_GATHER_PREFETCH = 0, 1
 
 DTYPES = {"fp16": ZS3_FP16, "bf16": ZS3_BF16}
 
@@ -44,7 +47,9 @@ EXPORTS = (
     "zs3_layout_param", "zs3_layout_own_range", "zs3_plan_buckets", "zs3_sub_groups",
     "zs3_bucket_sizes", "zs3_partition", "zs3_gather_coalesced", "zs3_reduce_scatter_local",
     "zs3_layout_norm_slots", "zs3_reduce_scatter_coalesced", "zs3_grad_norm", "zs3_grad_norm_partials",
-    "zs3_adam_step",
+    "zs3_adam_step", "zs3_coord_create", "zs3_coord_destroy", "zs3_coord_fetch", "zs3_coord_release",
+    "zs3_coord_release_all", "zs3_coord_reset_step", "zs3_coord_info", "zs3_coord_param_status",
+    "zs3_coord_trace_signature",
 )
 
 
@@ -53,6 +58,14 @@ class Zs3Error(RuntimeError):
         super().__init__(f"zs3 status {status}: {message}")
         self.status = status
         self.message = message
+
+
+class zs3_coord_config(ctypes.Structure):
+    _fields_ = [
+        ("prefetch_bucket_size", ctypes.c_int64),
+        ("max_live_parameters", ctypes.c_int64),
+        ("max_reuse_distance", ctypes.c_int64),
+    ]
 
 
 class zs3_adam_params(ctypes.Structure):
@@ -71,6 +84,8 @@ _c_i64 = ctypes.c_int64
 _c_p = ctypes.c_void_p
 _p_i64 = ctypes.POINTER(ctypes.c_int64)
 _p_i32 = ctypes.POINTER(ctypes.c_int32)
+
+_p_u64 = ctypes.POINTER(ctypes.c_uint64)
 
 _SIGNATURES = {
     "zs3_abi_version": (_c_i32, []),
@@ -100,6 +115,16 @@ _SIGNATURES = {
                                ctypes.c_double, _c_p, _c_p, _c_p, _c_p]),
     "zs3_adam_step": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
                                _c_p, _c_p, ctypes.POINTER(zs3_adam_params), _c_p]),
+    "zs3_coord_create": (_c_i32, [_c_p, _c_i32, _p_i32, _p_i64, ctypes.POINTER(zs3_coord_config),
+                                  ctypes.POINTER(_c_p)]),
+    "zs3_coord_destroy": (None, [_c_p]),
+    "zs3_coord_fetch": (_c_i32, [_c_p, _c_i32, _p_i32, _p_i32, _p_i32, _p_i64]),
+    "zs3_coord_release": (_c_i32, [_c_p, _c_i32, _p_i32, _p_i64]),
+    "zs3_coord_release_all": (_c_i32, [_c_p, _p_i32, _p_i64]),
+    "zs3_coord_reset_step": (_c_i32, [_c_p, _p_i32]),
+    "zs3_coord_info": (_c_i32, [_c_p, _p_i32, _p_i64, _p_i32, _p_i32]),
+    "zs3_coord_param_status": (_c_i32, [_c_p, _c_i64, _p_i32]),
+    "zs3_coord_trace_signature": (_c_i32, [_c_p, _p_u64, _p_u64, _p_i32]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -316,3 +341,87 @@ def zs3_adam_step(layout: int, rank: int, dtype, begin: int, end: int, master, e
     _check(lib().zs3_adam_step(layout, rank, _dtype(dtype), int(begin), int(end), _ptr(master), _ptr(exp_avg),
                                _ptr(exp_avg_sq), _ptr(grad_flat), _ptr(shard_flat), _ptr(scale), _ptr(nonfinite),
                                ctypes.byref(p), _stream(stream)))
+
+
+# ------------------------------------------------------------- coordinator
+
+_coord_cap = {}
+
+
+def _coord_cfg(cfg) -> zs3_coord_config:
+    if isinstance(cfg, zs3_coord_config):
+        return cfg
+    if isinstance(cfg, dict):
+        return zs3_coord_config(int(cfg["prefetch_bucket_size"]), int(cfg["max_live_parameters"]),
+                                int(cfg["max_reuse_distance"]))
+    return zs3_coord_config(int(cfg.prefetch_bucket_size), int(cfg.max_live_parameters), int(cfg.max_reuse_distance))
+
+
+def zs3_coord_create(layout: int, modules: Sequence[Sequence[int]], cfg) -> int:
+    """modules[m] = the ds_ids module m owns."""
+    starts = [0]
+    flat: List[int] = []
+    for m in modules:
+        flat += [int(d) for d in m]
+        starts.append(len(flat))
+    h = ctypes.c_void_p()
+    c = _coord_cfg(cfg)
+    _check(lib().zs3_coord_create(layout, len(modules), (ctypes.c_int32 * len(starts))(*starts), _i64s(flat),
+                                  ctypes.byref(c), ctypes.byref(h)))
+    _coord_cap[h.value] = max(1, len(flat))
+    return h.value
+
+
+def zs3_coord_destroy(coord: int) -> None:
+    _coord_cap.pop(coord, None)
+    lib().zs3_coord_destroy(coord)
+
+
+def zs3_coord_fetch(coord: int, module: int) -> List[Tuple[int, List[int]]]:
+    """[(kind, ds_ids), ...]: the gathers to issue, in order."""
+    n = ctypes.c_int32()
+    kinds = (ctypes.c_int32 * 2)()
+    starts = (ctypes.c_int32 * 3)()
+    ids = (ctypes.c_int64 * _coord_cap[coord])()
+    _check(lib().zs3_coord_fetch(coord, module, ctypes.byref(n), kinds, starts, ids))
+    return [(kinds[g], list(ids[starts[g]:starts[g + 1]])) for g in range(n.value)]
+
+
+def zs3_coord_release(coord: int, module: int) -> List[int]:
+    n = ctypes.c_int32()
+    ids = (ctypes.c_int64 * _coord_cap[coord])()
+    _check(lib().zs3_coord_release(coord, module, ctypes.byref(n), ids))
+    return list(ids[:n.value])
+
+
+def zs3_coord_release_all(coord: int) -> List[int]:
+    n = ctypes.c_int32()
+    ids = (ctypes.c_int64 * _coord_cap[coord])()
+    _check(lib().zs3_coord_release_all(coord, ctypes.byref(n), ids))
+    return list(ids[:n.value])
+
+
+def zs3_coord_reset_step(coord: int) -> int:
+    m = ctypes.c_int32()
+    _check(lib().zs3_coord_reset_step(coord, ctypes.byref(m)))
+    return m.value
+
+
+def zs3_coord_info(coord: int) -> dict:
+    m, t, inv = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    live = ctypes.c_int64()
+    _check(lib().zs3_coord_info(coord, ctypes.byref(m), ctypes.byref(live), ctypes.byref(t), ctypes.byref(inv)))
+    return {"mode": m.value, "live_numel": live.value, "trace_len": t.value, "invalidations": inv.value}
+
+
+def zs3_coord_param_status(coord: int, ds_id: int) -> int:
+    st = ctypes.c_int32()
+    _check(lib().zs3_coord_param_status(coord, int(ds_id), ctypes.byref(st)))
+    return st.value
+
+
+def zs3_coord_trace_signature(coord: int) -> Tuple[int, int, int]:
+    a, b = ctypes.c_uint64(), ctypes.c_uint64()
+    n = ctypes.c_int32()
+    _check(lib().zs3_coord_trace_signature(coord, ctypes.byref(a), ctypes.byref(b), ctypes.byref(n)))
+    return a.value, b.value, n.value

@@ -23,7 +23,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libzs3.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["kernels.hip", "api.cpp"]
+SOURCES = ["kernels.hip", "api.cpp", "coord.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

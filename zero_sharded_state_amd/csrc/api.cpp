@@ -119,6 +119,18 @@ constexpr size_t kMaxPlans = 1 << 14;
 
 }  // namespace
 
+struct zs3_layout;
+
+namespace zs3 {
+// Used by the coordinator (coord.cpp): the thread's last error, and a
+// parameter's facts by ds_id.
+zs3_status set_error(zs3_status s, const char* msg) {
+    g_last_error = msg;
+    return s;
+}
+bool layout_param(zs3_layout* L, int64_t ds_id, int64_t* numel, bool* persistent);
+}  // namespace zs3
+
 struct zs3_layout {
     int32_t world = 1;
     int64_t threshold = 0;
@@ -140,6 +152,14 @@ struct zs3_layout {
         plans.clear();
     }
 };
+
+bool zs3::layout_param(zs3_layout* L, int64_t ds_id, int64_t* numel, bool* persistent) {
+    auto it = L->index.find(ds_id);
+    if (it == L->index.end()) return false;
+    *numel = L->params[it->second].numel;
+    *persistent = L->params[it->second].persistent;
+    return true;
+}
 
 namespace {
 

@@ -339,15 +339,21 @@ class ShardStep:
                                             self.grad.data_ptr(), self.shard.data_ptr(), self.scale_ptr,
                                             self.flag_ptr, ctypes.byref(hp), s))
 
-    def step(self, stream=None, on_phase=None, gather_timer=None):
+    def step(self, stream=None, on_phase=None, gather_timer=None, trace_pass=None):
         """One whole shard step; ``on_phase(name)`` is called before each phase
-        and with None at the end (for event timing)."""
+        and with None at the end (for event timing).  With ``trace_pass`` (a
+        TraceGatherPass) the forward and backward gathers follow the
+        fetch/release coordinator instead of the static gather buckets."""
         self.t += 1
         mark = on_phase or (lambda name: None)
-        mark("gather_fwd")
-        self.gather_pass(stream, gather_timer)
-        mark("gather_bwd")
-        self.gather_pass(stream, gather_timer)
+        if trace_pass is not None:
+            mark("gather_trace")
+            trace_pass.run(stream)
+        else:
+            mark("gather_fwd")
+            self.gather_pass(stream, gather_timer)
+            mark("gather_bwd")
+            self.gather_pass(stream, gather_timer)
         mark("reduce_scatter")
         self.reduce_scatter(stream)
         mark("partition")
