@@ -57,6 +57,10 @@ def parse():
                     help="1: the reduce-scatter also writes the norm's partial sums (no second read of grad_flat)")
     ap.add_argument("--reduce-path", default="contiguous", choices=("contiguous", "coalesced"),
                     help="gradient path: all-reduced buckets (default) or reduce_scatter_coalesced")
+    ap.add_argument("--offload", type=int, default=0, choices=(0, 1),
+                    help="1: fp32 optimizer state in pinned host memory, streamed through the device per sub-group")
+    ap.add_argument("--offload-chunk", type=int, default=0,
+                    help="offloaded Adam: 0 reads the host state directly, else elements per staged chunk")
     ap.add_argument("--schedule", default="static", choices=("static", "trace"),
                     help="parameter gathers: static gather buckets twice (default), or the buckets the "
                          "trace-driven fetch/release coordinator returns over the forward+backward module order")
@@ -122,7 +126,8 @@ class KernelTimer:
             self.hip.hipEventDestroy(self.ct.c_void_p(b))
 
 
-def make_step(cfg, rank, rs_streams=1, gather_streams=1, fuse_norm=False, reduce_path="contiguous"):
+def make_step(cfg, rank, rs_streams=1, gather_streams=1, fuse_norm=False, reduce_path="contiguous", offload=False,
+              offload_chunk=0):
     from zero_sharded_state_amd.shard_step import AdamConfig, ShardStep
 
     return ShardStep(world_size=cfg.world_size, rank=rank, threshold=cfg.threshold, ds_ids=cfg.ds_ids,
@@ -130,7 +135,7 @@ def make_step(cfg, rank, rs_streams=1, gather_streams=1, fuse_norm=False, reduce
                      reduce_bucket_size=cfg.reduce_bucket_size, sub_group_size=cfg.sub_group_size,
                      adam=AdamConfig(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay),
                      max_norm=cfg.max_norm, rs_streams=rs_streams, gather_streams=gather_streams,
-                     fuse_norm=fuse_norm, reduce_path=reduce_path)
+                     fuse_norm=fuse_norm, reduce_path=reduce_path, offload=offload, offload_chunk=offload_chunk)
 
 
 def fill_inputs(step, cfg):
@@ -318,7 +323,8 @@ def main():
     cfg = get_config(args.config)
     rank = cfg.bench_rank if args.rank is None else args.rank
     log(f"config {cfg.name}: {cfg.title}, rank {rank}")
-    step = make_step(cfg, rank, args.rs_streams, args.gather_streams, bool(args.fuse_norm), args.reduce_path)
+    step = make_step(cfg, rank, args.rs_streams, args.gather_streams, bool(args.fuse_norm), args.reduce_path,
+                     bool(args.offload), args.offload_chunk)
     log(f"layout: S+P={step.S:,} own real={step.own_real:,} F={step.F:,} gather buckets={len(step.gather_buckets)} "
         f"reduce buckets={len(step.reduce_buckets)} sub-groups={len(step.sub_groups)}")
     t0 = time.time()
@@ -432,6 +438,13 @@ def main():
     coord = None
     if trace is not None:
         coord = coordinator_cost(step, cfg)
+    offload = None
+    if step.offload:
+        link = 24 * step.own_real            # fp32 master, momentum, variance: in and out once per step
+        ms = kernels["adam"]["ms"]
+        offload = {"link_bytes_per_step": link, "adam_ms": ms, "link_GBps": round(link / (ms * 1e-3) / 1e9, 1),
+                   "mode": "staged chunks of %d elements" % args.offload_chunk if args.offload_chunk else "direct",
+                   "note": "Adam phase with the fp32 state in pinned host memory, in and out over the host link"}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -465,13 +478,14 @@ def main():
             "sub_groups": len(step.sub_groups), "prefetch_bucket_size": cfg.prefetch_bucket_size,
             "reduce_bucket_size": cfg.reduce_bucket_size, "sub_group_size": cfg.sub_group_size,
             "reduce_path": step.reduce_path, "fused_norm": step.fuse_norm, "rs_streams": step.rs_streams,
-            "schedule": args.schedule,
+            "schedule": args.schedule, "offload": step.offload,
             "gather_streams": step.gather_streams,
         },
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "coordinator": coord,
+        "offload": offload,
         "source_digest": source_digest(),
     }
     print(json.dumps(line), flush=True)

@@ -363,6 +363,40 @@ ZS3_API zs3_status zs3_adam_step(zs3_layout_t layout, int32_t rank, int32_t dtyp
                          void* shard_flat, const float* scale, const int32_t* nonfinite,
                          const zs3_adam_params* hp, void* stream);
 
+/* -------------------------------- (f4) Adam on optimizer state held on the host
+ * [codex] 6.3: with the optimizer state offloaded, the per-sub-group step
+ * first swaps the sub-group's state in (_prepare_sub_group), steps it, writes
+ * the 16-bit shard, and swaps the state out again (_release_sub_group);
+ * [codex] 6.1: the fp32 partitions then live in host memory.
+ *
+ * Same update as zs3_adam_step over [begin, end) (bit-identical results),
+ * with master, exp_avg, exp_avg_sq in pinned host memory (host_*: whole
+ * flat arrays of shard_numel floats, allocated with hipHostMalloc or an
+ * equivalent pinned allocator that maps them for the device; other memory
+ * is rejected).  Two ways to move the state:
+ *   stage == NULL (direct): the kernel reads and writes the host arrays
+ *       through their device mapping on `stream`: each element's state
+ *       crosses the host link once in each direction, both directions at
+ *       once, with no staging buffer, copy or event.
+ *   stage != NULL (staged swap-in / swap-out): the range is streamed through
+ *       `stage` (dev, stage_elems floats, 16-byte aligned): two slots of
+ *       three arrays of chunk = floor((stage_elems/6 - 8)/8)*8 elements, so
+ *       at least 96 floats.  Per chunk: host-to-device copies on
+ *       copy_in_stream, the Adam kernel on `stream`, device-to-host copies
+ *       on copy_out_stream, so the copies of neighbouring chunks overlap
+ *       (either copy stream may be NULL: then `stream` carries it; copy
+ *       streams that share a hardware queue, or run kernels too, may
+ *       serialise the two directions).  The layout keeps the pipeline's
+ *       events: staged steps on one layout must not overlap.
+ * Ordering: the state is read after the work already on `stream`; when
+ * `stream` reaches the point after the call, every element is back in host
+ * memory.  The host must not touch the arrays meanwhile. */
+ZS3_API zs3_status zs3_adam_step_offload(zs3_layout_t layout, int32_t rank, int32_t dtype, int64_t begin,
+                                 int64_t end, float* host_master, float* host_exp_avg, float* host_exp_avg_sq,
+                                 float* stage, int64_t stage_elems, const void* grad_flat, void* shard_flat,
+                                 const float* scale, const int32_t* nonfinite, const zs3_adam_params* hp,
+                                 void* stream, void* copy_in_stream, void* copy_out_stream);
+
 /* ------------------------------------ (f2) trace-driven fetch/release plan
  * [codex] 5: a coordinator decides, module by module, which parameters to
  * all-gather and when to put them back in partitioned form.  Host only: no

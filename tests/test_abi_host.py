@@ -28,7 +28,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     syms = _declared_symbols()
-    assert len(syms) == 30
+    assert len(syms) == 31
     assert sorted(zs.EXPORTS) == syms
     for s in syms:
         assert hasattr(L, s), s
@@ -171,6 +171,28 @@ def test_call_validation_enqueues_nothing():
             (zs.ZS3_EINVAL, lambda: zs.zs3_grad_norm_partials(h, 0, base, base + 1 << 20, True, 0.0, 1.0,
                                                               base + 8192, base + 8200, base + 8204, stream=0)),
             (zs.ZS3_EALIAS, lambda: zs.zs3_grad_norm_partials(h, 0, base, base + 8, False, stream=0)),
+            # offloaded Adam: every check below runs before any HIP call
+            (zs.ZS3_EINVAL, lambda: zs.zs3_adam_step_offload(h, 0, "bf16", 0, S, base, base + (1 << 20),
+                                                             base + (2 << 20), base + (3 << 20), 95,
+                                                             base + (4 << 20), base + (5 << 20), base + (6 << 20),
+                                                             None, {"lr": 1e-3, "beta1": .9, "beta2": .999,
+                                                                    "eps": 1e-8, "step": 1}, stream=0)),
+            (zs.ZS3_EINVAL, lambda: zs.zs3_adam_step_offload(h, 0, "bf16", 0, S, 0, base + (1 << 20),
+                                                             base + (2 << 20), base + (3 << 20), 1 << 12,
+                                                             base + (4 << 20), base + (5 << 20), base + (6 << 20),
+                                                             None, {"lr": 1e-3, "beta1": .9, "beta2": .999,
+                                                                    "eps": 1e-8, "step": 1}, stream=0)),
+            (zs.ZS3_EALIAS, lambda: zs.zs3_adam_step_offload(h, 0, "bf16", 0, S, base, base + 4,
+                                                             base + (2 << 20), base + (3 << 20), 1 << 12,
+                                                             base + (4 << 20), base + (5 << 20), base + (6 << 20),
+                                                             None, {"lr": 1e-3, "beta1": .9, "beta2": .999,
+                                                                    "eps": 1e-8, "step": 1}, stream=0)),
+            (zs.ZS3_EALIAS, lambda: zs.zs3_adam_step_offload(h, 0, "bf16", 0, S, base, base + (1 << 20),
+                                                             base + (2 << 20), base + (3 << 20), 1 << 12,
+                                                             base + (3 << 20) + 64, base + (5 << 20),
+                                                             base + (6 << 20), None,
+                                                             {"lr": 1e-3, "beta1": .9, "beta2": .999,
+                                                              "eps": 1e-8, "step": 1}, stream=0)),
         ]
         for want, call in cases:
             with pytest.raises(zs.Zs3Error) as e:

@@ -6,7 +6,8 @@ over four streams).
   for 10 steps on the GPU against the oracle's own 10-step chain from the
   same synthetic inputs (weights, per-step gradients, the peers' norm
   partials); every output compared.  Variants: the norm fused into the
-  reduce, and the non-contiguous gradient path (reduce_scatter_coalesced).
+  reduce, the non-contiguous gradient path (reduce_scatter_coalesced), and
+  the optimizer state offloaded to pinned host memory.
 * c4 (Llama-3-8B set, 8.03B parameters, rank 0) and c5 (ragged 7.46B set,
   N = 64, rank 63, fp16, misaligned): each call fed fresh synthetic inputs,
   its outputs checked on a sample of whole parameters (the oracle recomputes
@@ -36,13 +37,14 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-def _step(cfg, rank, fuse_norm=False, reduce_path="contiguous"):
+def _step(cfg, rank, fuse_norm=False, reduce_path="contiguous", offload=False):
     from zero_sharded_state_amd.shard_step import AdamConfig, ShardStep
     return ShardStep(world_size=cfg.world_size, rank=rank, threshold=cfg.threshold, ds_ids=cfg.ds_ids,
                      numels=cfg.numels, dtype=cfg.dtype, prefetch_bucket_size=cfg.prefetch_bucket_size,
                      reduce_bucket_size=cfg.reduce_bucket_size, sub_group_size=cfg.sub_group_size,
                      adam=AdamConfig(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay),
-                     max_norm=cfg.max_norm, rs_streams=4, fuse_norm=fuse_norm, reduce_path=reduce_path)
+                     max_norm=cfg.max_norm, rs_streams=4, fuse_norm=fuse_norm, reduce_path=reduce_path,
+                     offload=bool(offload), offload_chunk=3_000_001 if offload == "staged" else 0)
 
 
 def h16(t):
@@ -99,16 +101,18 @@ def _oracle_reduce(step, L, cfg, rank, host_recv, host_own=None, host_x=None):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,rank,fuse_norm,reduce_path", [
-    ("c2", 0, False, "contiguous"), ("c2", 7, False, "contiguous"), ("c3", 0, False, "contiguous"),
-    ("c3", 7, False, "contiguous"), ("c2", 3, True, "contiguous"), ("c2", 7, True, "coalesced"),
-    ("c3", 0, True, "coalesced")])
-def test_chained_steps_match_oracle(name, rank, fuse_norm, reduce_path):
+@pytest.mark.parametrize("name,rank,fuse_norm,reduce_path,offload", [
+    ("c2", 0, False, "contiguous", False), ("c2", 7, False, "contiguous", False),
+    ("c3", 0, False, "contiguous", False), ("c3", 7, False, "contiguous", False),
+    ("c2", 3, True, "contiguous", False), ("c2", 7, True, "coalesced", False),
+    ("c3", 0, True, "coalesced", False), ("c2", 5, True, "contiguous", "staged"),
+    ("c3", 7, True, "contiguous", "direct")])
+def test_chained_steps_match_oracle(name, rank, fuse_norm, reduce_path, offload):
     import torch
     cfg = get_config(name)
     N, dt = cfg.world_size, cfg.dtype
-    note(f"chain {name} rank={rank} fuse_norm={fuse_norm} {reduce_path}: set-up")
-    step = _step(cfg, rank, fuse_norm, reduce_path)
+    note(f"chain {name} rank={rank} fuse_norm={fuse_norm} {reduce_path} offload={offload}: set-up")
+    step = _step(cfg, rank, fuse_norm, reduce_path, offload)
     L = oracle.make_layout(N, cfg.threshold, cfg.ds_ids, cfg.numels)
     try:
         full = {d: weights_host(cfg, d) for d in cfg.ds_ids}

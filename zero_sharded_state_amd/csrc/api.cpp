@@ -140,8 +140,16 @@ struct zs3_layout {
     std::vector<int64_t> slot_base;                 // first norm slot of each parameter (layout order)
     int64_t n_slots = 0, n_part_slots = 0;
     std::unordered_map<Key, Plan, KeyHash> plans;
+    std::unordered_map<int, std::vector<hipEvent_t>> events;   // per device: the offload pipeline's events
 
-    ~zs3_layout() { release_plans(); }
+    ~zs3_layout() {
+        release_plans();
+        if (!events.empty()) {
+            (void)hipDeviceSynchronize();
+            for (auto& kv : events)
+                for (hipEvent_t e : kv.second) (void)hipEventDestroy(e);
+        }
+    }
 
     void release_plans() {
         if (plans.empty()) return;
@@ -436,6 +444,87 @@ zs3_status check_partials(const zs3_layout* L, const double* partials, const voi
     if (overlap(partials, 8 * L->n_slots, grad_flat, 2 * L->shard_numel))
         return fail(ZS3_EALIAS, "partials overlaps grad_flat");
     return ZS3_OK;
+}
+
+}  // namespace
+
+namespace {
+
+AdamConsts adam_consts(const zs3_adam_params* hp) {
+    AdamConsts c;
+    const double t = static_cast<double>(hp->step);
+    c.lr = static_cast<float>(hp->lr);
+    c.b1 = static_cast<float>(hp->beta1);
+    c.b2 = static_cast<float>(hp->beta2);
+    c.omb1 = static_cast<float>(1.0 - hp->beta1);
+    c.omb2 = static_cast<float>(1.0 - hp->beta2);
+    c.bc1 = static_cast<float>(1.0 - std::pow(hp->beta1, t));
+    c.bc2 = static_cast<float>(1.0 - std::pow(hp->beta2, t));
+    c.eps = static_cast<float>(hp->eps);
+    c.lrwd = static_cast<float>(hp->lr * hp->weight_decay);
+    c.has_wd = hp->weight_decay != 0.0 ? 1 : 0;
+    return c;
+}
+
+// The Adam launch over [begin, end) of the flat arrays (validated by the caller).
+zs3_status adam_launch(zs3_layout* L, int32_t rank, int32_t dtype, int64_t begin, int64_t end, float* master,
+                       float* exp_avg, float* exp_avg_sq, const void* grad_flat, void* shard_flat, const float* scale,
+                       const int32_t* nonfinite, const AdamConsts& c, void* stream) {
+    zs3_status s;
+    const bool vec_ok = aligned(master, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16) &&
+                        aligned(grad_flat, 16) && aligned(shard_flat, 16);
+    Key key{{kOpAdam, device_id(), rank, begin, end}};
+    Plan* plan = find_plan(L, key);
+    if (plan == nullptr) {
+        // real runs of [begin, end): padding positions are skipped
+        std::vector<std::pair<int64_t, int64_t>> runs;
+        for (const Slot& p : L->params) {
+            const int64_t a = std::max(begin, p.offset);
+            const int64_t b = std::min(end, p.offset + p.real(rank));
+            if (b <= a) continue;
+            if (!runs.empty() && runs.back().first + runs.back().second == a) runs.back().second += b - a;
+            else runs.emplace_back(a, b - a);
+        }
+        std::vector<Span> spans;
+        for (auto& r : runs) add_spans(&spans, r.first, r.second, (8 - (r.first & 7)) & 7, kAdamPiece);
+        if ((s = check_grid(static_cast<int64_t>(spans.size()), kAdamSub)) != ZS3_OK) return s;
+        Plan np;
+        np.n_pieces = static_cast<int64_t>(spans.size());
+        if (runs.size() <= static_cast<size_t>(kAdamInlineRuns)) {
+            auto ai = std::make_shared<AdamInline>();
+            std::memset(ai.get(), 0, sizeof(AdamInline));
+            ai->nrun = static_cast<int32_t>(runs.size());
+            int32_t np_ = 0;
+            size_t si = 0;
+            for (size_t i = 0; i < runs.size(); ++i) {
+                ai->piece_start[i] = np_;
+                ai->begin[i] = runs[i].first;
+                ai->count[i] = runs[i].second;
+                // spans of run i are consecutive in `spans`
+                while (si < spans.size() && spans[si].begin < runs[i].first + runs[i].second) {
+                    ++np_;
+                    ++si;
+                }
+            }
+            ai->piece_start[runs.size()] = np_;
+            np.adam_inline = std::move(ai);
+        } else {
+            std::vector<size_t> offs;
+            s = upload(&np, {{spans.data(), spans.size() * sizeof(Span)}}, 0, &offs);
+            if (s != ZS3_OK) return s;
+            np.off_pieces = offs[0];
+        }
+        store_plan(L, std::move(key), std::move(np), &plan);
+    }
+    if (plan->adam_inline)
+        return hip_status(launch_adam_inline(dtype, *plan->adam_inline, master, exp_avg, exp_avg_sq,
+                                             static_cast<const uint16_t*>(grad_flat), static_cast<uint16_t*>(shard_flat),
+                                             scale, nonfinite, c, vec_ok, static_cast<hipStream_t>(stream)),
+                          "Adam kernel launch");
+    return hip_status(launch_adam(dtype, plan->at<Span>(plan->off_pieces), plan->n_pieces, master, exp_avg, exp_avg_sq,
+                                  static_cast<const uint16_t*>(grad_flat), static_cast<uint16_t*>(shard_flat), scale,
+                                  nonfinite, c, vec_ok, static_cast<hipStream_t>(stream)),
+                      "Adam kernel launch");
 }
 
 }  // namespace
@@ -1088,73 +1177,122 @@ zs3_status zs3_adam_step(zs3_layout_t L, int32_t rank, int32_t dtype, int64_t be
             if (overlap(arr[i], bytes[i], arr[j], bytes[j])) return fail(ZS3_EALIAS, "Adam arrays %d and %d overlap", i, j);
     if (nb == 0) return ok();
 
-    AdamConsts c;
-    const double t = static_cast<double>(hp->step);
-    c.lr = static_cast<float>(hp->lr);
-    c.b1 = static_cast<float>(hp->beta1);
-    c.b2 = static_cast<float>(hp->beta2);
-    c.omb1 = static_cast<float>(1.0 - hp->beta1);
-    c.omb2 = static_cast<float>(1.0 - hp->beta2);
-    c.bc1 = static_cast<float>(1.0 - std::pow(hp->beta1, t));
-    c.bc2 = static_cast<float>(1.0 - std::pow(hp->beta2, t));
-    c.eps = static_cast<float>(hp->eps);
-    c.lrwd = static_cast<float>(hp->lr * hp->weight_decay);
-    c.has_wd = hp->weight_decay != 0.0 ? 1 : 0;
+    return adam_launch(L, rank, dtype, begin, end, master, exp_avg, exp_avg_sq, grad_flat, shard_flat, scale,
+                       nonfinite, adam_consts(hp), stream);
+}
 
-    const bool vec_ok = aligned(master, 16) && aligned(exp_avg, 16) && aligned(exp_avg_sq, 16) &&
-                        aligned(grad_flat, 16) && aligned(shard_flat, 16);
-    Key key{{kOpAdam, device_id(), rank, begin, end}};
-    Plan* plan = find_plan(L, key);
-    if (plan == nullptr) {
-        // real runs of [begin, end): padding positions are skipped
-        std::vector<std::pair<int64_t, int64_t>> runs;
-        for (const Slot& p : L->params) {
-            const int64_t a = std::max(begin, p.offset);
-            const int64_t b = std::min(end, p.offset + p.real(rank));
-            if (b <= a) continue;
-            if (!runs.empty() && runs.back().first + runs.back().second == a) runs.back().second += b - a;
-            else runs.emplace_back(a, b - a);
-        }
-        std::vector<Span> spans;
-        for (auto& r : runs) add_spans(&spans, r.first, r.second, (8 - (r.first & 7)) & 7, kAdamPiece);
-        if ((s = check_grid(static_cast<int64_t>(spans.size()), kAdamSub)) != ZS3_OK) return s;
-        Plan np;
-        np.n_pieces = static_cast<int64_t>(spans.size());
-        if (runs.size() <= static_cast<size_t>(kAdamInlineRuns)) {
-            auto ai = std::make_shared<AdamInline>();
-            std::memset(ai.get(), 0, sizeof(AdamInline));
-            ai->nrun = static_cast<int32_t>(runs.size());
-            int32_t np_ = 0;
-            size_t si = 0;
-            for (size_t i = 0; i < runs.size(); ++i) {
-                ai->piece_start[i] = np_;
-                ai->begin[i] = runs[i].first;
-                ai->count[i] = runs[i].second;
-                // spans of run i are consecutive in `spans`
-                while (si < spans.size() && spans[si].begin < runs[i].first + runs[i].second) {
-                    ++np_;
-                    ++si;
-                }
-            }
-            ai->piece_start[runs.size()] = np_;
-            np.adam_inline = std::move(ai);
-        } else {
-            std::vector<size_t> offs;
-            s = upload(&np, {{spans.data(), spans.size() * sizeof(Span)}}, 0, &offs);
-            if (s != ZS3_OK) return s;
-            np.off_pieces = offs[0];
-        }
-        store_plan(L, std::move(key), std::move(np), &plan);
+// ------------------------------------------------- (f4) offloaded Adam
+
+zs3_status zs3_adam_step_offload(zs3_layout_t L, int32_t rank, int32_t dtype, int64_t begin, int64_t end,
+                                 float* host_master, float* host_exp_avg, float* host_exp_avg_sq, float* stage,
+                                 int64_t stage_elems, const void* grad_flat, void* shard_flat, const float* scale,
+                                 const int32_t* nonfinite, const zs3_adam_params* hp, void* stream,
+                                 void* copy_in_stream, void* copy_out_stream) {
+    zs3_status s = check_layout_rank(L, rank);
+    if (s != ZS3_OK) return s;
+    if ((s = check_dtype(dtype)) != ZS3_OK) return s;
+    if (hp == nullptr) return fail(ZS3_EINVAL, "hp is NULL");
+    if (hp->step < 1) return fail(ZS3_EINVAL, "step %lld < 1", (long long)hp->step);
+    if (begin < 0 || end < begin || end > L->shard_numel)
+        return fail(ZS3_EINVAL, "range [%lld, %lld) outside [0, %lld]", (long long)begin, (long long)end,
+                    (long long)L->shard_numel);
+    float* host[3] = {host_master, host_exp_avg, host_exp_avg_sq};
+    const int64_t nb = end - begin;
+    for (int i = 0; i < 3; ++i) {
+        if (host[i] == nullptr || !aligned(host[i], 4)) return fail(ZS3_EINVAL, "host state array %d is NULL or misaligned", i);
+        for (int j = 0; j < i; ++j)
+            if (overlap(host[i] + begin, 4 * nb, host[j] + begin, 4 * nb))
+                return fail(ZS3_EALIAS, "host state arrays %d and %d overlap", j, i);
     }
-    if (plan->adam_inline)
-        return hip_status(launch_adam_inline(dtype, *plan->adam_inline, master, exp_avg, exp_avg_sq,
-                                             static_cast<const uint16_t*>(grad_flat), static_cast<uint16_t*>(shard_flat),
-                                             scale, nonfinite, c, vec_ok, static_cast<hipStream_t>(stream)),
-                          "Adam kernel launch");
-    return hip_status(launch_adam(dtype, plan->at<Span>(plan->off_pieces), plan->n_pieces, master, exp_avg, exp_avg_sq,
-                                  static_cast<const uint16_t*>(grad_flat), static_cast<uint16_t*>(shard_flat), scale,
-                                  nonfinite, c, vec_ok, static_cast<hipStream_t>(stream)),
-                      "Adam kernel launch");
+    // staged: two slots of three arrays, each chunk + 8 elements (alignment room)
+    const bool staged = stage != nullptr;
+    const int64_t chunk = staged ? (stage_elems / 6 - 8) / 8 * 8 : 0;
+    if (staged && !aligned(stage, 16)) return fail(ZS3_EINVAL, "stage is not 16-byte aligned");
+    if (staged && chunk < 8) return fail(ZS3_EINVAL, "stage of %lld elements is too small (at least 96)", (long long)stage_elems);
+    if (scale == nullptr || !aligned(scale, 4) || (nonfinite != nullptr && !aligned(nonfinite, 4)))
+        return fail(ZS3_EINVAL, "scale is NULL, or scale or nonfinite is misaligned");
+    if ((s = check_ptr16(grad_flat, "grad_flat")) != ZS3_OK) return s;
+    if ((s = check_ptr16(shard_flat, "shard_flat")) != ZS3_OK) return s;
+    const int64_t stage_bytes = staged ? 4 * 6 * (chunk + 8) : 0;
+    if (overlap(stage, stage_bytes, static_cast<const uint16_t*>(grad_flat) + begin, 2 * nb) ||
+        overlap(stage, stage_bytes, static_cast<uint16_t*>(shard_flat) + begin, 2 * nb) ||
+        overlap(static_cast<const uint16_t*>(grad_flat) + begin, 2 * nb, static_cast<uint16_t*>(shard_flat) + begin, 2 * nb))
+        return fail(ZS3_EALIAS, "stage, grad_flat and shard_flat overlap");
+    if (nb == 0) return ok();
+    float* mapped[3];
+    for (int i = 0; i < 3; ++i) {
+        hipPointerAttribute_t a;
+        if (hipPointerGetAttributes(&a, host[i]) != hipSuccess || a.type != hipMemoryTypeHost ||
+            a.devicePointer == nullptr) {
+            (void)hipGetLastError();
+            return fail(ZS3_EINVAL, "host state array %d is not pinned host memory mapped for the device", i);
+        }
+        mapped[i] = static_cast<float*>(a.devicePointer);
+    }
+    if (!staged) {
+        // direct: the kernel reads and writes the host arrays through their
+        // device mapping, so the state crosses the link once each way with
+        // no copy engine, staging buffer or event in between
+        return adam_launch(L, rank, dtype, begin, end, mapped[0], mapped[1], mapped[2], grad_flat, shard_flat, scale,
+                           nonfinite, adam_consts(hp), stream);
+    }
+
+    const int dev = device_id();
+    auto& ev = L->events[dev];
+    if (ev.empty()) {
+        for (int i = 0; i < 7; ++i) {
+            hipEvent_t e;
+            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+                (void)hipGetLastError();
+                for (hipEvent_t x : ev) (void)hipEventDestroy(x);
+                ev.clear();
+                return fail(ZS3_EHIP, "hipEventCreate failed");
+            }
+            ev.push_back(e);
+        }
+    }
+    hipStream_t cs = static_cast<hipStream_t>(stream);
+    hipStream_t in = copy_in_stream ? static_cast<hipStream_t>(copy_in_stream) : cs;
+    hipStream_t out = copy_out_stream ? static_cast<hipStream_t>(copy_out_stream) : cs;
+    hipEvent_t ev_start = ev[0], ev_in[2] = {ev[1], ev[2]}, ev_done[2] = {ev[3], ev[4]}, ev_out[2] = {ev[5], ev[6]};
+    const AdamConsts c = adam_consts(hp);
+    auto hip = [](hipError_t e, const char* what) { return hip_status(e, what); };
+
+    // the copies start after everything already on the compute stream
+    if ((s = hip(hipEventRecord(ev_start, cs), "event record")) != ZS3_OK) return s;
+    if ((s = hip(hipStreamWaitEvent(in, ev_start, 0), "stream wait")) != ZS3_OK) return s;
+    const int64_t n_chunks = (nb + chunk - 1) / chunk;
+    bool used[2] = {false, false};
+    for (int64_t i = 0; i < n_chunks; ++i) {
+        const int64_t b = begin + i * chunk, e = std::min(end, b + chunk), n = e - b;
+        const int slot = static_cast<int>(i & 1);
+        float* base = stage + static_cast<int64_t>(slot) * 3 * (chunk + 8);
+        const int64_t off = b & 7;      // keeps (slot array - b) 16-byte aligned, as the kernel's vector path needs
+        float* dv[3] = {base + off, base + (chunk + 8) + off, base + 2 * (chunk + 8) + off};
+        // _prepare_sub_group: swap in (after the slot's previous swap-out)
+        if (used[slot] && (s = hip(hipStreamWaitEvent(in, ev_out[slot], 0), "stream wait")) != ZS3_OK) return s;
+        for (int a = 0; a < 3; ++a)
+            if ((s = hip(hipMemcpyAsync(dv[a], host[a] + b, 4 * n, hipMemcpyHostToDevice, in), "swap-in copy")) != ZS3_OK)
+                return s;
+        if ((s = hip(hipEventRecord(ev_in[slot], in), "event record")) != ZS3_OK) return s;
+        // _optimizer_step on the staged partition
+        if ((s = hip(hipStreamWaitEvent(cs, ev_in[slot], 0), "stream wait")) != ZS3_OK) return s;
+        if ((s = adam_launch(L, rank, dtype, b, e, dv[0] - b, dv[1] - b, dv[2] - b, grad_flat, shard_flat, scale,
+                             nonfinite, c, stream)) != ZS3_OK)
+            return s;
+        if ((s = hip(hipEventRecord(ev_done[slot], cs), "event record")) != ZS3_OK) return s;
+        // _release_sub_group: swap out
+        if ((s = hip(hipStreamWaitEvent(out, ev_done[slot], 0), "stream wait")) != ZS3_OK) return s;
+        for (int a = 0; a < 3; ++a)
+            if ((s = hip(hipMemcpyAsync(host[a] + b, dv[a], 4 * n, hipMemcpyDeviceToHost, out), "swap-out copy")) != ZS3_OK)
+                return s;
+        if ((s = hip(hipEventRecord(ev_out[slot], out), "event record")) != ZS3_OK) return s;
+        used[slot] = true;
+    }
+    // the call is complete on the compute stream once both slots are swapped out
+    for (int slot = 0; slot < 2; ++slot)
+        if (used[slot] && (s = hip(hipStreamWaitEvent(cs, ev_out[slot], 0), "stream wait")) != ZS3_OK) return s;
+    return ok();
 }
 
 }  // extern "C"

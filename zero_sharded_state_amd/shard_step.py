@@ -54,7 +54,8 @@ class ShardStep:
                  numels: Sequence[int], dtype: str, prefetch_bucket_size: int, reduce_bucket_size: int,
                  sub_group_size: int, adam: AdamConfig = AdamConfig(), max_norm: float = 1.0,
                  device: str = "cuda", rs_streams: int = 1, gather_streams: int = 1,
-                 fuse_norm: bool = False, reduce_path: str = "contiguous"):
+                 fuse_norm: bool = False, reduce_path: str = "contiguous", offload: bool = False,
+                 offload_chunk: int = 0):
         import torch
 
         if reduce_path not in ("contiguous", "coalesced"):
@@ -110,9 +111,19 @@ class ShardStep:
         self.grad = torch.zeros(max(1, self.S), dtype=i16, device=dev)
         self.recv = torch.zeros(max(1, self.N * self.S), dtype=i16, device=dev)  # slices sent to this rank
         # the fp32 optimizer partition (master, momentum, variance) is one
-        # allocation, each array starting on a 2 MiB boundary
+        # allocation, each array starting on a 2 MiB boundary; offloaded, it
+        # lives in pinned host memory and Adam streams it through a device
+        # staging buffer ([codex] 6.1, 6.3)
         sa = (max(1, self.S) + (1 << 19) - 1) >> 19 << 19
-        self.state = torch.zeros(3 * sa, dtype=f32, device=dev)
+        self.offload = bool(offload)
+        if self.offload:
+            # offload_chunk 0: Adam reads and writes the host state directly;
+            # otherwise chunks of that many elements are staged through HBM
+            self.state = torch.zeros(3 * sa, dtype=f32, pin_memory=True)
+            self.stage_elems = 6 * (int(offload_chunk) + 8) if offload_chunk else 0
+            self.stage = torch.empty(self.stage_elems, dtype=f32, device=dev) if offload_chunk else None
+        else:
+            self.state = torch.zeros(3 * sa, dtype=f32, device=dev)
         self.master = self.state[0:max(1, self.S)]
         self.exp_avg = self.state[sa:sa + max(1, self.S)]
         self.exp_avg_sq = self.state[2 * sa:2 * sa + max(1, self.S)]
@@ -125,8 +136,13 @@ class ShardStep:
         self.t = 0
         # independent gradient buckets are spread over a few streams so that
         # short reduce-scatter kernels overlap (default priority streams)
-        n_aux = max(0, max(rs_streams, gather_streams) - 1)
+        # (the offloaded Adam's swap-in and swap-out copies use two of them:
+        # a process has few hardware queues, and streams that share one
+        # serialise, so no stream is created just for the copies)
+        n_aux = max(0, max(rs_streams, gather_streams, 3 if self.offload and offload_chunk else 0) - 1)
         self.aux_streams = [torch.cuda.Stream(device=dev) for _ in range(n_aux)]
+        if self.offload:
+            self.copy_streams = self.aux_streams[:2]
         self.rs_streams = max(1, rs_streams)
         self.gather_streams = max(1, gather_streams)
         self._fork = torch.cuda.Event()
@@ -333,6 +349,15 @@ class ShardStep:
         a = self.adam
         hp = zs.zs3_adam_params(a.lr, a.beta1, a.beta2, a.eps, a.weight_decay, int(t))
         s = stream if stream is not None else self._stream()
+        if self.offload:
+            cin, cout = (int(x.cuda_stream) for x in self.copy_streams) if self.stage is not None else (None, None)
+            for b, e in self.sub_groups:
+                self._ok(zs.lib().zs3_adam_step_offload(
+                    self.h, self.rank, self.dcode, b, e, self.master.data_ptr(), self.exp_avg.data_ptr(),
+                    self.exp_avg_sq.data_ptr(), self.stage.data_ptr() if self.stage is not None else None,
+                    self.stage_elems, self.grad.data_ptr(),
+                    self.shard.data_ptr(), self.scale_ptr, self.flag_ptr, ctypes.byref(hp), s, cin, cout))
+            return
         for b, e in self.sub_groups:
             self._ok(zs.lib().zs3_adam_step(self.h, self.rank, self.dcode, b, e, self.master.data_ptr(),
                                             self.exp_avg.data_ptr(), self.exp_avg_sq.data_ptr(),
