@@ -208,7 +208,7 @@ def test_call_validation_enqueues_nothing():
         zs.zs3_layout_destroy(h)
 
 
-def _slot_count(ps_list, piece=256 * 8 * 8, per_piece=8 * 4):
+def _slot_count(ps_list, piece=256 * 2 * 8 * 8, per_piece=8 * 4):
     return sum(per_piece * (1 if ps <= piece else -(-ps // piece)) for ps in ps_list)
 
 

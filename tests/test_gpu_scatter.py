@@ -221,7 +221,7 @@ def test_fused_norm_every_slot_written_at_piece_edges(shift):
     destination alignment: the spare slot group is zeroed when the aligned
     split needs one piece fewer than the bound."""
     import torch
-    P = 256 * 8 * 8     # elements of one reduce-scatter piece
+    P = 256 * 2 * 8 * 8     # elements of one reduce-scatter piece (256 threads x 2 vectors x 8 x 8 workgroups)
     numels = [1, 7, 8, 9, P - 1, P, P + 1, P + 2, P + 7, P + 8, 2 * P + 3, 3 * P - 1]
     ids = list(range(len(numels)))
     h, L = _layout(ids, numels, 1, 0)

@@ -23,7 +23,7 @@ constexpr int kBlock = 256;             // threads per workgroup (4 wave64)
 #define ZS3_COPY_SUB 4
 #endif
 #ifndef ZS3_RS_VPT
-#define ZS3_RS_VPT 1
+#define ZS3_RS_VPT 2
 #endif
 #ifndef ZS3_RS_SUB
 #define ZS3_RS_SUB 8
