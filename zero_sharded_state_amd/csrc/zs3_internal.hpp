@@ -41,7 +41,7 @@ constexpr int kBlock = 256;             // threads per workgroup (4 wave64)
 #define ZS3_ADAM_GPT 1
 #endif
 #ifndef ZS3_ADAM_SUB
-#define ZS3_ADAM_SUB 4
+#define ZS3_ADAM_SUB 8
 #endif
 // Non-temporal hints per family: on MI355X they help the copies, the
 // reduce-scatter and the norm, and slow the Adam pass (measured).
