@@ -310,7 +310,7 @@ def coordinator_cost(step, cfg, steps: int = 5):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the N data-parallel ranks are virtual "
+        print(json.dumps({"error": "bench.py measures one GPU only: the N data-parallel ranks are virtual "
                                    "ranks in one GPU's HBM; --gpus must be 1", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     import torch
