@@ -9,9 +9,11 @@ over four streams).
   reduce, the non-contiguous gradient path (reduce_scatter_coalesced), and
   the optimizer state offloaded to pinned host memory.
 * c4 (Llama-3-8B set, 8.03B parameters, rank 0) and c5 (ragged 7.46B set,
-  N = 64, rank 63, fp16, misaligned): each call fed fresh synthetic inputs,
-  its outputs checked on a sample of whole parameters (the oracle recomputes
-  those parameters only) or, for the norm, over the whole buffer.
+  N = 64, rank 63, fp16, misaligned), in bench.py's launch configuration
+  (three gradient streams, fused norm): each call fed fresh synthetic
+  inputs, its outputs checked on a sample of whole parameters (the oracle
+  recomputes those parameters only) or, for the norm, over the whole flat
+  gradient the reduce-scatter produced.
 """
 
 import gc
@@ -43,7 +45,7 @@ def _step(cfg, rank, fuse_norm=False, reduce_path="contiguous", offload=False):
                      numels=cfg.numels, dtype=cfg.dtype, prefetch_bucket_size=cfg.prefetch_bucket_size,
                      reduce_bucket_size=cfg.reduce_bucket_size, sub_group_size=cfg.sub_group_size,
                      adam=AdamConfig(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay),
-                     max_norm=cfg.max_norm, rs_streams=4, fuse_norm=fuse_norm, reduce_path=reduce_path,
+                     max_norm=cfg.max_norm, rs_streams=3, fuse_norm=fuse_norm, reduce_path=reduce_path,
                      offload=bool(offload), offload_chunk=3_000_001 if offload == "staged" else 0)
 
 
@@ -207,12 +209,14 @@ def _sample_params(L, cfg, k=6):
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["c4", "c5"])
 def test_fullsize_calls_on_sampled_parameters(name):
+    """In bench.py's launch configuration: gradient buckets over three
+    streams, the norm fused into the reduce-scatter."""
     import torch
     cfg = get_config(name)
     rank = cfg.bench_rank
     N, dt = cfg.world_size, cfg.dtype
     note(f"fullsize {name} rank={rank}: set-up")
-    step = _step(cfg, rank)
+    step = _step(cfg, rank, fuse_norm=True)
     L = oracle.make_layout(N, cfg.threshold, cfg.ds_ids, cfg.numels)
     sample = _sample_params(L, cfg)
     dev = step.device
@@ -279,17 +283,14 @@ def test_fullsize_calls_on_sampled_parameters(name):
             oracle.reduce_scatter(sub, rank, dt, [d], grads, ref)
             assert np.array_equal(gh[p.shard_offset:p.shard_offset + p.partition_size], ref), f"reduce-scatter {d}"
 
-        # ---- norm: synthetic flat gradient (padding zero) -> partial sums, norm, scale
-        device_normal16(step.S, 1e-3, dt, dev, (cfg.seed, cfg.config_id, KIND_GRAD, 2), out=step.grad)
-        pad = oracle.padding_mask(L, rank)
-        if pad.any():
-            step.grad[torch.from_numpy(pad).to(dev)] = 0
+        # ---- norm: the partial sums the reduce-scatter just wrote, over the
+        # whole flat gradient it produced -> norm and scale
         peers = np.random.default_rng(5).uniform(0.5, 2.0, N)
         step.sumsq.copy_(torch.from_numpy(np.append(peers, 0.0)))
         note(f"fullsize {name}: grad norm")
         step.grad_norm()
         sync()
-        gflat = h16(step.grad)
+        gflat = gh
         a, q = oracle.grad_norm_partial(L, rank, dt, gflat)
         parts = list(peers)
         parts[rank] = a

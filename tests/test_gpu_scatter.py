@@ -266,3 +266,45 @@ def test_fused_norm_nonfinite_flag():
         assert int(outs.cpu().numpy()[1:2].view(np.int32)[1]) == 1
     finally:
         zs.zs3_layout_destroy(h)
+
+
+def test_fused_norm_on_an_empty_layout():
+    """No parameters: no slots; the partial sums are 0 and the peers' sums
+    alone make the norm."""
+    import torch
+    h = zs.zs3_layout_create(2, 0, [], [])
+    try:
+        assert zs.zs3_layout_norm_slots(h) == (0, 0)
+        partials = torch.zeros(1, dtype=torch.float64, device="cuda")
+        sumsq = torch.full((3,), 7.0, dtype=torch.float64, device="cuda")
+        sumsq[1] = 4.0
+        outs = torch.zeros(2, dtype=torch.float64, device="cuda")
+        zs.zs3_grad_norm_partials(h, 0, partials, sumsq, True, 1.0, 1.0, outs.data_ptr(), outs.data_ptr() + 8,
+                                  outs.data_ptr() + 12)
+        sync()
+        s = sumsq.cpu().numpy()
+        assert s[0] == 0.0 and s[2] == 0.0 and float(outs.cpu().numpy()[0]) == 2.0
+    finally:
+        zs.zs3_layout_destroy(h)
+
+
+def test_scatter_empty_request_and_padding_only_rank():
+    """An empty bucket is a no-op; a rank whose ranges are all padding
+    writes zeros (and zero partial sums) whatever the chunks hold."""
+    import torch
+    h = zs.zs3_layout_create(64, 0, [0, 1], [5, 70])      # rank 63: padding of both (ps 1 and 2)
+    try:
+        zs.zs3_reduce_scatter_coalesced(h, 63, "fp16", zs.ZS3_PACK | zs.ZS3_REDUCE, [], grads=[], send=Buf16(8).ptr(),
+                                        recv_chunks=[Buf16(8).ptr()] * 64, grad_flat=Buf16(8).ptr())
+        n_slots, _ = zs.zs3_layout_norm_slots(h)
+        partials = torch.full((n_slots,), float("nan"), dtype=torch.float64, device="cuda")
+        chunks = [Buf16(3, fill=np.array([0x3C00, 0x3C00, 0x3C00], np.uint16)) for _ in range(64)]
+        out = Buf16(3, fill=np.full(3, 0x1234, np.uint16))
+        zs.zs3_reduce_scatter_coalesced(h, 63, "fp16", zs.ZS3_REDUCE, [1, 0], recv_chunks=[c.ptr() for c in chunks],
+                                        grad_flat=out.ptr(), partials=partials.data_ptr())
+        sync()
+        assert out.host().tolist() == [0, 0, 0]
+        assert np.all(partials.cpu().numpy() == 0.0)
+        out.check_guards()
+    finally:
+        zs.zs3_layout_destroy(h)
