@@ -250,8 +250,9 @@ __device__ __forceinline__ int find_seg(const int32_t (&piece_start)[MAXSEG + 1]
     return s;
 }
 
-// One body, four kernel names (partition, pack, unpack, fused gather) so
-// that profiles attribute time to each step of the method.  Two ways to
+// One body, five kernel names (partition, pack, unpack, fused gather, the
+// non-contiguous path's send-side pack) so that profiles attribute time to
+// each step of the method.  Two ways to
 // find the work: a device work list (k_copy) or, for calls with few
 // segments, the whole plan in the kernel arguments (k_copy_inline), which
 // saves the dependent loads of the list at the start of every launch.
@@ -473,9 +474,11 @@ __device__ __forceinline__ int64_t piece_index(int64_t begin, int64_t head) {
     return begin == 0 ? 0 : 1 + (begin - head - kRsPiece) / kRsPiece;
 }
 
-// The workgroup's partial sum goes to slot + q*kRsSub + sub; the last piece
-// of a slice that needs one piece fewer than the slot bound also zeroes the
-// spare group.
+// The partial sums of piece q, sub-block `sub` go to slot group q: one slot
+// per workgroup (a workgroup sum) or, by default, one per wave (each wave's
+// own sum, no barrier) at slot + (q*kRsSub + sub)*kSlotsPerWG + wave.  The
+// last piece of a slice that needs one piece fewer than the slot bound also
+// zeroes the spare group.
 __device__ __forceinline__ void put_partial(double ss, double* partials, int64_t slot, int64_t q, int64_t actual,
                                             int64_t total, int sub, double* sh) {
     const bool spare = q == actual - 1 && actual < norm_slot_groups(total);
