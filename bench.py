@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -69,11 +70,21 @@ def parse():
     return ap.parse_args()
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments and with whitespace collapsed, so that a
+    comment or layout edit does not count as a change of the kernels.
+    (String literals are left alone; none of these files has // or /* in one.)"""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest() -> str:
+    """Digest of the code the kernels and their launch plans are built from."""
     h = hashlib.sha256()
     for f in ("kernels.hip", "api.cpp", "zs3_internal.hpp"):
-        with open(os.path.join(ROOT, "zero_sharded_state_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "zero_sharded_state_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
