@@ -10,6 +10,13 @@ data-parallel ranks are N virtual ranks in this GPU's HBM; inputs are
 synthetic (seeded N(0, 0.02) weights, N(0, 1e-3) gradients with 1% x100
 outliers) and resident in HBM before timing starts.
 
+Default launch configuration: gather buckets back to back on one stream,
+gradient buckets over three streams, the norm fused into the reduce.
+Variants: --reduce-path coalesced (the non-contiguous gradient path),
+--schedule trace (gathers driven by the fetch/release coordinator over the
+forward+backward module order), --offload 1 (the fp32 optimizer state in
+pinned host memory), --fuse-norm 0, --rs-streams N.
+
 Prints ONE JSON line: effective HBM GB/s of the step (its fixed algorithmic
 byte budget / time: 2 x (pack + unpack) + reduce-scatter + re-partition +
 norm + Adam, the same for every variant, so a variant that fuses away a

@@ -1,9 +1,10 @@
 """One rank's ZeRO-3 shard step, with the N data-parallel ranks held as N
 virtual ranks in one GPU's HBM.
 
-The step issues, on one stream, the calls a real rank makes around its
-collectives, in the order the pages give ([llmnex] section 2, [codex]
-5.2, 6.2, 6.3):
+The step issues the calls a real rank makes around its collectives, in the
+order the pages give ([llmnex] section 2, [codex] 5.2, 6.2, 6.3), on one
+stream (the gradient buckets, whose outputs are disjoint, may be dealt over
+a few streams that fork from it and join back):
 
 1. forward all-gather of every gather bucket: pack the own shard into the
    rank's chunk of the bucket's wire buffer, then unpack the N chunks into
@@ -25,7 +26,8 @@ collectives, in the order the pages give ([llmnex] section 2, [codex]
    unchanged);
 5. the global gradient norm and clip scale ([llmnex] pitfall 1), from
    grad_flat or, with ``fuse_norm``, from the reduce's partial sums;
-6. fused Adam + cast per sub-group.
+6. fused Adam + cast per sub-group, on the fp32 state in HBM or, with
+   ``offload``, in pinned host memory ([codex] 6.1, 6.3).
 
 No call synchronises; nothing is copied to the host.  All buffers are torch
 tensors owned by this object; all arithmetic runs in libzs3's kernels.
@@ -112,8 +114,7 @@ class ShardStep:
         self.recv = torch.zeros(max(1, self.N * self.S), dtype=i16, device=dev)  # slices sent to this rank
         # the fp32 optimizer partition (master, momentum, variance) is one
         # allocation, each array starting on a 2 MiB boundary; offloaded, it
-        # lives in pinned host memory and Adam streams it through a device
-        # staging buffer ([codex] 6.1, 6.3)
+        # lives in pinned host memory ([codex] 6.1, 6.3)
         sa = (max(1, self.S) + (1 << 19) - 1) >> 19 << 19
         self.offload = bool(offload)
         if self.offload:
