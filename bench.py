@@ -166,7 +166,7 @@ def fill_inputs(step, cfg):
     if step.P:
         device_normal16(step.P, cfg.weight_std, cfg.dtype, dev, (cfg.seed, cfg.config_id, KIND_WEIGHT, 1),
                         out=step.pers_full)
-    device_normal16(step.N * step.S, cfg.grad_std, cfg.dtype, dev, (cfg.seed, cfg.config_id, KIND_GRAD, step.rank),
+    device_normal16(step.recv.numel(), cfg.grad_std, cfg.dtype, dev, (cfg.seed, cfg.config_id, KIND_GRAD, step.rank),
                     outlier_prob=cfg.outlier_prob, outlier_mult=cfg.outlier_mult, out=step.recv)
     if step.reduce_path == "coalesced":
         # the rank's own full gradients and the chunks its peers send it
@@ -231,7 +231,7 @@ def cpu_baseline(step, cfg, layers: int):
             p = step.by_id[d]
             lo, hi = p["own"]
             a = np.zeros(p["numel"], np.uint16)
-            o = v * step.S + p["shard_offset"]
+            o = v * step.recv_stride + p["shard_offset"]
             a[lo:hi] = h16(step.recv[o:o + (hi - lo)])
             g[d] = a
         grads.append(g)

@@ -61,7 +61,7 @@ def _recv_grads(step, L, host_recv):
     """Oracle-side gradients: virtual rank v's full gradient of every
     parameter, zero except the slice this rank receives (the oracle reads
     only that slice)."""
-    N, S = step.N, step.S
+    N, S = step.N, step.recv_stride
     grads = []
     for v in range(N):
         g = {}
@@ -135,7 +135,7 @@ def test_chained_steps_match_oracle(name, rank, fuse_norm, reduce_path, offload)
         peers = np.random.default_rng(cfg.config_id).uniform(0.5, 2.0, N) * 1e-3   # what the all-reduce delivers
         for t in range(1, cfg.steps + 1):
             note(f"chain {name} rank={rank}: step {t}")
-            device_normal16(step.N * step.S, cfg.grad_std, dt, step.device, (cfg.seed, cfg.config_id, KIND_GRAD, t),
+            device_normal16(step.recv.numel(), cfg.grad_std, dt, step.device, (cfg.seed, cfg.config_id, KIND_GRAD, t),
                             outlier_prob=cfg.outlier_prob, outlier_mult=cfg.outlier_mult, out=step.recv)
             host_recv = h16(step.recv)
             host_own = host_x = None
@@ -262,7 +262,7 @@ def test_fullsize_calls_on_sampled_parameters(name):
             assert np.array_equal(own, ch[rank]), f"packed chunk of bucket {bi}"
 
         # ---- reduce-scatter: synthetic received slices -> flat gradient
-        device_normal16(step.N * step.S, cfg.grad_std, dt, dev, (cfg.seed, cfg.config_id, KIND_GRAD, 1),
+        device_normal16(step.recv.numel(), cfg.grad_std, dt, dev, (cfg.seed, cfg.config_id, KIND_GRAD, 1),
                         outlier_prob=cfg.outlier_prob, outlier_mult=cfg.outlier_mult, out=step.recv)
         note(f"fullsize {name}: reduce-scatter")
         step.grad.fill_(0x3C3C)
@@ -275,7 +275,7 @@ def test_fullsize_calls_on_sampled_parameters(name):
             grads = []
             for v in range(N):
                 a = np.zeros(p.numel, np.uint16)
-                o = v * step.S + p.shard_offset
+                o = v * step.recv_stride + p.shard_offset
                 a[lo:hi] = h16(step.recv[o:o + (hi - lo)])
                 grads.append({d: a})
             sub = oracle.make_layout(N, cfg.threshold, [d], [p.numel])

@@ -352,12 +352,59 @@ struct InlineSrcs {
     __device__ __forceinline__ const uint16_t* operator()(int v) const { return plan.src[base + v]; }
 };
 
+// Ragged ends are summed with 2-byte loads (a source may end at its last
+// real element, so no 16-byte load may run past it).  The loads of
+// kRsBatch sources are issued together and then added in rank order, so a
+// thread waits for memory world/kRsBatch times instead of world times.
 template <int D, class SRC>
 __device__ __forceinline__ uint16_t rs_elem(const SRC& sp, int world, Divider div, int64_t k, int64_t real) {
     if (k >= real) return 0;
     float acc = 0.0f;
-    for (int v = 0; v < world; ++v) acc += widen<D>(sp(v)[k]);
+    for (int vb = 0; vb < world; vb += kRsBatch) {
+        uint32_t x[kRsBatch];
+#pragma unroll
+        for (int j = 0; j < kRsBatch; ++j)
+            if (vb + j < world) x[j] = sp(vb + j)[k];
+#pragma unroll
+        for (int j = 0; j < kRsBatch; ++j)
+            if (vb + j < world) acc += widen<D>(x[j]);
+    }
     return static_cast<uint16_t>(narrow<D>(div(acc)));
+}
+
+// The 8 elements [k, k + 8) of a vector that ends the real part or lies
+// past it: its real elements with 2-byte loads, all 8 elements of a batch
+// of sources in flight together, zeros for the padding.
+template <int D, bool NORM, class SRC>
+__device__ __forceinline__ void rs_tail_vector(uint16_t* dst, const SRC& sp, int world, Divider div, int64_t k,
+                                               int64_t real, double& ss) {
+    int64_t ne = real - k;
+    if (ne < 0) ne = 0;
+    if (ne > 8) ne = 8;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    if (ne > 0) {
+        for (int vb = 0; vb < world; vb += kRsBatch) {
+            uint32_t x[kRsBatch][8];
+#pragma unroll
+            for (int j = 0; j < kRsBatch; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (vb + j < world && e < ne) x[j][e] = sp(vb + j)[k + e];
+#pragma unroll
+            for (int j = 0; j < kRsBatch; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (vb + j < world && e < ne) acc[e] += widen<D>(x[j][e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint16_t x = e < ne ? static_cast<uint16_t>(narrow<D>(div(acc[e]))) : uint16_t(0);
+        dst[e] = x;
+        if constexpr (NORM) ss += sq_fast<D>(x);
+    }
 }
 
 // Writes one element and, with NORM, adds the square of what was written.
@@ -455,9 +502,7 @@ __device__ __forceinline__ double rs_piece(const SRC& sp, uint16_t* seg_dst, int
     int64_t lo = i0 > nfull ? i0 : nfull;
     int64_t hi = i0 + int64_t(kBlock) * kRsVPT;
     if (hi > nv) hi = nv;
-    for (int64_t i = lo + t; i < hi; i += kBlock) {
-        for (int e = 0; e < 8; ++e) rs_put<D, NORM>(dst + 8 * i + e, sp, world, div, k0 + 8 * i + e, real, ss);
-    }
+    for (int64_t i = lo + t; i < hi; i += kBlock) rs_tail_vector<D, NORM>(dst + 8 * i, sp, world, div, k0 + 8 * i, real, ss);
     const int64_t rem = n & 7;
     if (sub == kRsSub - 1 && t < rem) rs_put<D, NORM>(dst + nv * 8 + t, sp, world, div, k0 + nv * 8 + t, real, ss);
     return ss;

@@ -111,7 +111,12 @@ class ShardStep:
         self.wire = torch.empty(max(1, self.W), dtype=i16, device=dev)        # per-bucket all-gather output
         self.shard = torch.zeros(max(1, self.S), dtype=i16, device=dev)
         self.grad = torch.zeros(max(1, self.S), dtype=i16, device=dev)
-        self.recv = torch.zeros(max(1, self.N * self.S), dtype=i16, device=dev)  # slices sent to this rank
+        # the slices the N ranks send this rank, laid out like the flat shard,
+        # one per rank at a stride rounded up to 8 elements: every source of
+        # an element then has the byte address of its grad_flat destination
+        # modulo 16 (the reduce-scatter's co-aligned 128-bit path)
+        self.recv_stride = (self.S + 7) // 8 * 8
+        self.recv = torch.zeros(max(1, self.N * self.recv_stride), dtype=i16, device=dev)
         # the fp32 optimizer partition (master, momentum, variance) is one
         # allocation, each array starting on a 2 MiB boundary; offloaded, it
         # lives in pinned host memory ([codex] 6.1, 6.3)
@@ -163,7 +168,7 @@ class ShardStep:
 
     def recv_ptr(self, v: int, ds_id: int) -> int:
         """Where virtual rank v's slice of parameter ds_id for this rank lives."""
-        return self.recv.data_ptr() + 2 * (v * self.S + self.by_id[ds_id]["shard_offset"])
+        return self.recv.data_ptr() + 2 * (v * self.recv_stride + self.by_id[ds_id]["shard_offset"])
 
     def _coalesced_buffers(self):
         """Own full gradients, per-bucket send buffers and received chunks.
