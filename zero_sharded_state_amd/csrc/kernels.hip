@@ -95,31 +95,37 @@ __device__ __forceinline__ int64_t head16(const void* p) {
     return static_cast<int64_t>(((16u - (static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)) & 15u)) & 15u) >> 1);
 }
 
+// The 16 bytes that start SO bytes into the aligned block `lo` and run on
+// into the next aligned block `hi` (16-bit data, SO even, 0 < SO < 16).
+template <int SO>
+__device__ __forceinline__ v4u shift_pair(v4u lo, v4u hi) {
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    constexpr int d = SO / 4;
+    v4u r;
+    if constexpr (SO % 4 == 0) {
+        r.x = w[d]; r.y = w[d + 1]; r.z = w[d + 2]; r.w = w[d + 3];
+    } else {
+        r.x = __builtin_amdgcn_alignbyte(w[d + 1], w[d], 2);
+        r.y = __builtin_amdgcn_alignbyte(w[d + 2], w[d + 1], 2);
+        r.z = __builtin_amdgcn_alignbyte(w[d + 3], w[d + 2], 2);
+        r.w = __builtin_amdgcn_alignbyte(w[d + 4], w[d + 3], 2);
+    }
+    return r;
+}
+
 // 16 bytes of 16-bit data starting at p, whose byte address is SO (mod 16).
 // SO != 0 reads the two aligned 16-byte blocks that hold those bytes and
 // shifts; both blocks contain bytes of the requested range, so neither can
-// cross into a page the range does not touch.  (Plain loads: the second
-// block is the next lane's first and should hit in cache.)
+// cross into a page the range does not touch.  (The second block is the
+// next lane's first and should hit in cache; non-temporal loads of both
+// measured 5% slower.)
 template <int SO, bool NT>
 __device__ __forceinline__ v4u load_shift(const uint16_t* p) {
     if constexpr (SO == 0) {
         return ld_stream<NT>(p);
     } else {
         const v4u* a = reinterpret_cast<const v4u*>(reinterpret_cast<uintptr_t>(p) - SO);
-        const v4u lo = a[0];
-        const v4u hi = a[1];
-        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        constexpr int d = SO / 4;
-        v4u r;
-        if constexpr (SO % 4 == 0) {
-            r.x = w[d]; r.y = w[d + 1]; r.z = w[d + 2]; r.w = w[d + 3];
-        } else {
-            r.x = __builtin_amdgcn_alignbyte(w[d + 1], w[d], 2);
-            r.y = __builtin_amdgcn_alignbyte(w[d + 2], w[d + 1], 2);
-            r.z = __builtin_amdgcn_alignbyte(w[d + 3], w[d + 2], 2);
-            r.w = __builtin_amdgcn_alignbyte(w[d + 4], w[d + 3], 2);
-        }
-        return r;
+        return shift_pair<SO>(a[0], a[1]);
     }
 }
 
@@ -152,10 +158,43 @@ template <int SO>
 __device__ __forceinline__ void copy_body(const uint16_t* src, uint16_t* dst, uint16_t* dst2, int64_t n2,
                                           int64_t i0, int64_t nv, int t) {
     v4u r[kCopyVPT];
+    if constexpr (SO != 0) {
+        // The lanes of a wave hold consecutive vectors, so a lane's second
+        // block is the next lane's first: one load per lane, the second
+        // block from a shuffle, and a load of its own only where there is no
+        // next lane (the wave's last lane, the piece's last vector).  All
+        // loads are issued before the first shuffle waits.  (Measured on
+        // ragged fp16 gathers: 2% faster than two loads per lane.)
+        const int lane = t & 63;
+        v4u lo[kCopyVPT], hi[kCopyVPT];
 #pragma unroll
-    for (int u = 0; u < kCopyVPT; ++u) {
-        const int64_t i = i0 + t + int64_t(u) * kBlock;
-        if (i < nv) r[u] = load_shift<SO, kNtCopy>(src + 8 * i);
+        for (int u = 0; u < kCopyVPT; ++u) {
+            const int64_t i = i0 + t + int64_t(u) * kBlock;
+            const v4u* a = reinterpret_cast<const v4u*>(reinterpret_cast<uintptr_t>(src + 8 * i) - SO);
+            lo[u] = v4u{0u, 0u, 0u, 0u};
+            hi[u] = v4u{0u, 0u, 0u, 0u};
+            if (i < nv) {
+                lo[u] = ld_stream<kNtCopy>(a);
+                if (lane == 63 || i + 1 >= nv) hi[u] = ld_stream<kNtCopy>(a + 1);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyVPT; ++u) {
+            const int64_t i = i0 + t + int64_t(u) * kBlock;
+            v4u nx;
+            nx.x = static_cast<uint32_t>(__shfl_down(static_cast<int>(lo[u].x), 1, 64));
+            nx.y = static_cast<uint32_t>(__shfl_down(static_cast<int>(lo[u].y), 1, 64));
+            nx.z = static_cast<uint32_t>(__shfl_down(static_cast<int>(lo[u].z), 1, 64));
+            nx.w = static_cast<uint32_t>(__shfl_down(static_cast<int>(lo[u].w), 1, 64));
+            if (!(lane == 63 || i + 1 >= nv)) hi[u] = nx;
+            r[u] = shift_pair<SO>(lo[u], hi[u]);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kCopyVPT; ++u) {
+            const int64_t i = i0 + t + int64_t(u) * kBlock;
+            if (i < nv) r[u] = load_shift<SO, kNtCopy>(src + 8 * i);
+        }
     }
 #pragma unroll
     for (int u = 0; u < kCopyVPT; ++u) {
