@@ -25,15 +25,19 @@
  *   - Host arrays ("host") are read before the call returns.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call that
  *     takes a stream only enqueues work on it and returns; none
- *     synchronises.  Outputs are ready when the stream reaches that point.
+ *     synchronises (except the first use of a call shape and a full table
+ *     cache, below).  Outputs are ready when the stream reaches that point.
  *   - All arguments are validated before any work is enqueued: on an error
  *     nothing is enqueued and the return value says why; zs3_last_error()
  *     gives a message (thread-local).  Nothing throws across the ABI.
  *   - A layout caches small device tables (segment and work lists, keyed by
  *     the call's parameters and pointers).  The first call with a new key
  *     allocates and uploads its table synchronously; later identical calls
- *     reuse it.  Cached tables are freed only by zs3_layout_destroy, which
- *     first waits for the device to go idle.
+ *     reuse it.  Cached tables are freed by zs3_layout_destroy, which first
+ *     waits for the device to go idle, and when a layout already holds
+ *     16384 of them: the next call with a new key then waits for the
+ *     device to go idle and frees them all before it builds its own (the
+ *     only case in which a call synchronises).
  *   - Calls on one layout from several host threads must be serialised by
  *     the caller.  zs3_grad_norm and zs3_grad_norm_partials keep
  *     per-layout scratch: two norm calls on one layout that overlap on
