@@ -27,9 +27,12 @@
  *     takes a stream only enqueues work on it and returns; none
  *     synchronises (except the first use of a call shape and a full table
  *     cache, below).  Outputs are ready when the stream reaches that point.
- *   - All arguments are validated before any work is enqueued: on an error
- *     nothing is enqueued and the return value says why; zs3_last_error()
- *     gives a message (thread-local).  Nothing throws across the ABI.
+ *   - All arguments are validated before any work is enqueued: on an
+ *     argument error nothing is enqueued and the return value says why;
+ *     zs3_last_error() gives a message (thread-local).  A HIP or allocation
+ *     failure (ZS3_EHIP, ZS3_ENOMEM) in a call that launches several kernels
+ *     (separate pack and unpack, pack and reduce, the offload pipeline) may
+ *     leave the earlier launches enqueued.  Nothing throws across the ABI.
  *   - A layout caches small device tables (segment and work lists, keyed by
  *     the call's parameters and pointers).  The first call with a new key
  *     allocates and uploads its table synchronously; later identical calls
