@@ -188,6 +188,52 @@ def test_reduce_scatter_bit_exact(prob, dtype, slice_only, shift):
         zs.zs3_layout_destroy(h)
 
 
+# Gradient values whose fp32 sums depend on the order of the adds (sums
+# reach past 24 significant bits and round, often on ties): the kernel's
+# rank-order sum must match the oracle's bit for bit.
+ORDER_VALUES = {
+    "bf16": [0x4B80, 0xCB80, 0x3F80, 0xBF80, 0x4B00, 0xCB00, 0x3F00, 0x4C00, 0xCC00, 0x0000, 0x8000, 0x3E80],
+    "fp16": [0x7800, 0xF800, 0x1800, 0x9800, 0x3C00, 0xBC00, 0x7400, 0xF400, 0x1400, 0x0001, 0x8000, 0x6800],
+}
+
+
+@pytest.mark.parametrize("N", [3, 8, 9, 64])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_reduce_scatter_order_sensitive_values(N, dtype):
+    from oracle import brute
+    ids, numels, T = [4, 9, 13], [3 * 32768 + 13, 40000, 999], 0
+    rng = np.random.default_rng(N)
+    vals = np.array(ORDER_VALUES[dtype], np.uint16)
+    grads = [{d: rng.choice(vals, nm) for d, nm in zip(ids, numels)} for _ in range(N)]
+    h, L = _layout(ids, numels, N, T)
+    try:
+        for r in sorted({0, N - 1}):
+            p0 = L.slot(ids[0])
+            lo, hi = L.own_range(p0, r)
+            sample = [[int(grads[v][ids[0]][lo + k]) for v in range(N)] for k in range(min(200, hi - lo))]
+            flips = sum(brute.reduce_scatter_elem(x, dtype) != brute.reduce_scatter_elem(x[::-1], dtype)
+                        for x in sample)
+            assert flips > 0, "the input does not depend on the order of the adds"
+            ref = np.zeros(L.shard_numel, np.uint16)
+            oracle.reduce_scatter(L, r, dtype, ids, grads, ref)
+            note(f"reduce_scatter order-sensitive N={N} rank={r} {dtype}")
+            out = Buf16(L.shard_numel, fill=np.full(L.shard_numel, 0x3C3C, np.uint16))
+            keep, src = [], []
+            for d in ids:
+                lo, hi = L.own_range(L.slot(d), r)
+                for v in range(N):
+                    buf = Buf16(hi - lo, shift=v % 8, fill=grads[v][d][lo:hi]) if hi > lo else None
+                    keep.append(buf)
+                    src.append(buf.ptr() if buf is not None else 0)
+            zs.zs3_reduce_scatter_local(h, r, dtype, ids, src, out.ptr())
+            sync()
+            got = out.host()
+            assert np.array_equal(got, ref), f"mismatch at {np.nonzero(got != ref)[0][:10]}"
+            out.check_guards()
+    finally:
+        zs.zs3_layout_destroy(h)
+
+
 def test_reduce_scatter_worked_example():
     """The csdn page's 4-GPU example: grads 0.5, 1, 1.5, 2 on every rank;
     GPU r keeps the averaged unit it owns (GPU0: 0.5)."""

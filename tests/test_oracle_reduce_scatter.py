@@ -134,3 +134,43 @@ def test_concatenated_slices_equal_dense_average():
         d = np.abs(_ordinal(cat, cfg.dtype) - _ordinal(ref, cfg.dtype))
         assert d.max() <= 1
         assert (d == 0).mean() > 0.99
+
+
+# Values whose fp32 sum depends on the order of the adds: in rank order the
+# middle value is lost to a tie rounded to even, so the sum is exactly 0;
+# in reverse order it survives.  bf16: 2^24, 1, -2^24 (2^24 + 1 needs 25
+# significant bits).  fp16: 2^15, 2^-9, -2^15 (2^-9 is half an fp32 ulp of
+# 2^15).
+ORDER_TRIPLES = {
+    "bf16": ([0x4B80, 0x3F80, 0xCB80], 1.0),
+    "fp16": ([0x7800, 0x1800, 0xF800], 2.0 ** -9),
+}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_rank_order_of_the_sum_is_observable(dtype):
+    """Reading of [csdn] step 3 / [codex] 6.2 (the pages give only "sum, then
+    average"): the fp32 sum runs over the ranks in rank order.  With the
+    triple above every rank's averaged element is exactly +0; the reverse
+    order would give the small value divided by 3."""
+    bits, small = ORDER_TRIPLES[dtype]
+    N = 3
+    L = oracle.make_layout(N, 0, [0], [N])          # one element per rank
+    grads = [{0: np.full(N, bits[v], np.uint16)} for v in range(N)]
+    outs = _rs_all(L, dtype, grads)
+    assert [int(o[0]) for o in outs] == [0x0000] * N
+    assert brute.reduce_scatter_elem(bits, dtype) == 0x0000
+    rev = brute.reduce_scatter_elem(bits[::-1], dtype)
+    assert brute.value16(rev, dtype) == pytest.approx(small / 3, rel=2 ** -7)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_sum_starts_at_positive_zero(dtype):
+    """The fp32 sum starts at +0: when every rank's gradient is -0 the
+    average is +0 (a sum seeded with the first rank's value would give -0)."""
+    N = 4
+    L = oracle.make_layout(N, 0, [0], [2 * N])
+    grads = [{0: np.full(2 * N, 0x8000, np.uint16)} for _ in range(N)]
+    for o in _rs_all(L, dtype, grads):
+        assert o.tolist() == [0x0000, 0x0000]
+    assert brute.reduce_scatter_elem([0x8000] * N, dtype) == 0x0000
