@@ -31,9 +31,11 @@ Modules:
 * ``coordinator`` -- the trace-driven fetch/release coordinator as a
   step-by-step simulation (imported as ``oracle.coordinator``).
 
-Parity status of each function is stated in its docstring; the only
-function without an independent pin is the decoupled weight-decay branch of
-``adam_step`` ("parity unpinned": every workload uses weight_decay = 0).
+Parity status of each function is stated in its docstring; every function
+has an independent pin.  (The decoupled weight-decay branch of
+``adam_step``, which the pages never mention and every workload leaves at
+weight_decay = 0, is pinned against torch.optim.AdamW, a zero-gradient
+closed form and the per-element brute force.)
 """
 
 from .zero3 import (  # noqa: F401

@@ -163,12 +163,16 @@ def sumsq(bits: Sequence[int], dtype: str) -> float:
 
 
 def adam_elem(w: float, m: float, v: float, gbits: int, dtype: str, scale: float,
-              lr: float, b1: float, b2: float, eps: float, t: int):
-    """One element of one Adam step, every operation rounded to fp32."""
+              lr: float, b1: float, b2: float, eps: float, t: int, wd: float = 0.0):
+    """One element of one Adam step, every operation rounded to fp32.  A
+    non-zero ``wd`` first shrinks the weight by lr * wd, decoupled from the
+    gradient (Loshchilov & Hutter's AdamW)."""
     c_lr, c_b1, c_b2, c_eps = f32(lr), f32(b1), f32(b2), f32(eps)
     omb1, omb2 = f32(1.0 - b1), f32(1.0 - b2)
     bc1, bc2 = f32(1.0 - b1 ** t), f32(1.0 - b2 ** t)
     g = f32(value16(gbits, dtype) * scale)
+    if wd != 0.0:
+        w = f32(w - f32(f32(lr * wd) * w))
     m = f32(f32(c_b1 * m) + f32(omb1 * g))
     v = f32(f32(c_b2 * v) + f32(omb2 * f32(g * g)))
     mh = f32(m / bc1)

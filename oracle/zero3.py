@@ -488,7 +488,7 @@ def adam_step(layout: Layout, rank: int, dtype: str, begin: int, end: int,
     print no formula).  Each line below is one fp32 operation:
 
         g   = f32(grad16) * scale
-        w   = w - lrwd * w               (only if weight_decay != 0; unpinned)
+        w   = w - lrwd * w               (only if weight_decay != 0: decoupled, as in AdamW)
         m   = b1 * m + omb1 * g
         v   = b2 * v + omb2 * (g * g)
         mh  = m / bc1 ;  vh = v / bc2

@@ -203,7 +203,12 @@ def _adam_with(slip):
         if slip != "unscaled":
             g = g * np.float32(scale)
         if hp.weight_decay != 0.0:
-            w = w - c["lrwd"] * w
+            if slip == "wd_coupled":
+                g = g + np.float32(hp.weight_decay) * w
+            elif slip == "wd_without_lr":
+                w = w - np.float32(hp.weight_decay) * w
+            else:
+                w = w - c["lrwd"] * w
         if slip == "beta_swap":
             m = c["b2"] * m + c["omb2"] * g
         elif slip == "fma":
@@ -289,6 +294,8 @@ MUTANTS = {
     "adam_updates_padding": lambda n: _set("adam_step", _adam_with("padding")),
     "adam_fused_multiply_add": lambda n: _set("adam_step", _adam_with("fma")),
     "adam_reordered_update": lambda n: _set("adam_step", _adam_with("reordered")),
+    "adam_weight_decay_coupled_into_gradient": lambda n: _set("adam_step", _adam_with("wd_coupled")),
+    "adam_weight_decay_without_lr": lambda n: _set("adam_step", _adam_with("wd_without_lr")),
     "bf16_rounding_by_truncation": lambda n: _set("from_f32", _from_f32_bf16_truncate(z.from_f32)),
     "fp16_subnormals_flushed": lambda n: _set("to_f32", _to_f32_fp16_flush(z.to_f32)),
 }

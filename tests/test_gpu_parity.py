@@ -315,6 +315,16 @@ def test_grad_norm_nonfinite_flag():
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("shift", [0, 1])
 def test_adam_ten_steps(prob, dtype, shift):
+    _adam_chain(prob, dtype, shift, 0.0)
+
+
+@pytest.mark.parametrize("prob", [PROBLEMS[2], PROBLEMS[4], PROBLEMS[5]])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_adam_ten_steps_with_weight_decay(prob, dtype):
+    _adam_chain(prob, dtype, 1, 0.05)
+
+
+def _adam_chain(prob, dtype, shift, wd):
     import torch
     seed, N, T, n, mx = prob
     ids, numels, full = _problem(seed, N, T, n, mx, dtype)
@@ -334,8 +344,8 @@ def test_adam_ten_steps(prob, dtype, shift):
             G = Buf16(L.shard_numel, shift, g)
             scale = np.float32(0.8 if t % 2 else 1.0)
             scal[0] = float(scale)
-            hp = oracle.AdamHParams(1e-3, 0.9, 0.999, 1e-8, 0.0, t)
-            note(f"adam seed={seed} N={N} rank={r} {dtype} shift={shift} step={t}")
+            hp = oracle.AdamHParams(1e-3, 0.9, 0.999, 1e-8, wd, t)
+            note(f"adam seed={seed} N={N} rank={r} {dtype} shift={shift} wd={wd} step={t}")
             for b, e in groups:
                 oracle.adam_step(L, r, dtype, b, e, w, m, v, g, shard, scale, False, hp)
                 zs.zs3_adam_step(h, r, dtype, b, e, W.ptr(), M.ptr(), V.ptr(), G.ptr(), S.ptr(),

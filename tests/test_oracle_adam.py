@@ -55,8 +55,9 @@ def test_worked_example_after_one_step():
     assert oracle.to_f32(shard, "fp16").tolist() == [0.9990234375, 1.9990234375, 2.998046875, 3.998046875]
 
 
+@pytest.mark.parametrize("wd", [0.0, 0.01])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-def test_matches_pure_python_fp32_emulation(dtype):
+def test_matches_pure_python_fp32_emulation(dtype, wd):
     rng = np.random.default_rng(9)
     n = 64
     w16 = to16_host(rng.standard_normal(n).astype(np.float32) * np.float32(0.02), dtype)
@@ -69,11 +70,11 @@ def test_matches_pure_python_fp32_emulation(dtype):
     for t in range(1, 4):
         g16 = to16_host(rng.standard_normal(n).astype(np.float32) * np.float32(1e-3), dtype)
         scale = np.float32(0.8125)
-        hp = oracle.AdamHParams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, step=t)
+        hp = oracle.AdamHParams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=wd, step=t)
         oracle.adam_step(L, 0, dtype, 0, n, master, m, v, g16, shard, scale, False, hp)
         for i in range(n):
             bw[i], bm[i], bv[i], sb = brute.adam_elem(bw[i], bm[i], bv[i], int(g16[i]), dtype,
-                                                      float(scale), 1e-3, 0.9, 0.999, 1e-8, t)
+                                                      float(scale), 1e-3, 0.9, 0.999, 1e-8, t, wd)
             assert int(shard[i]) == sb
         assert master.tolist() == bw and m.tolist() == bm and v.tolist() == bv
 
@@ -111,6 +112,67 @@ def test_agrees_with_torch_adam():
     assert np.max(np.abs(master.astype(np.float64) - tw)) <= 10 * (2e-6 * 1e-3) + 4 * np.max(_ulp32(w0))
     moved = np.abs(master.astype(np.float64) - w0)
     assert moved.min() > 0 and moved.max() <= 10 * 1e-3 * 1.0001
+
+
+@pytest.mark.parametrize("wd", [0.01, 0.1])
+def test_weight_decay_with_zero_gradient_closed_form(wd):
+    """Decoupled weight decay (Loshchilov & Hutter): with a zero gradient the
+    moments stay 0, the Adam term is lr * (0 / eps) = 0, and one step only
+    shrinks the weight: w1 = w0 * (1 - lr * wd), to within one fp32 rounding
+    of each of the two operations.  (L2 decay folded into the gradient would
+    move every weight by about lr instead.)"""
+    rng = np.random.default_rng(21)
+    n = 4096
+    w0 = (rng.standard_normal(n) * 0.5).astype(np.float32)
+    L = oracle.make_layout(1, 0, [0], [n])
+    w, m, v = w0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    shard = oracle.from_f32(w0, "bf16")
+    lr = 1e-3
+    oracle.adam_step(L, 0, "bf16", 0, n, w, m, v, np.zeros(n, np.uint16), shard, np.float32(1.0), False,
+                     oracle.AdamHParams(lr=lr, weight_decay=wd, step=1))
+    exact = w0.astype(np.float64) * (1.0 - lr * wd)
+    assert np.all(np.abs(w - exact) <= 1.5 * _ulp32(w0))
+    assert np.all(m == 0) and np.all(v == 0)
+    assert np.array_equal(shard, oracle.from_f32(w, "bf16"))
+    assert np.all(np.abs(w) < np.abs(w0)) or np.all(w0 == 0)
+
+
+def test_agrees_with_torch_adamw():
+    """torch.optim.AdamW shrinks the weight by lr * weight_decay before the
+    Adam update, as the oracle does; agreement to rounding over 10 steps."""
+    rng = np.random.default_rng(4)
+    n = 50000
+    wd = 0.1
+    w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    L = oracle.make_layout(1, 0, [0], [n])
+    master = w0.copy()
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    shard = oracle.from_f32(w0, "bf16")
+    p = torch.nn.Parameter(torch.from_numpy(w0.copy()))
+    opt = torch.optim.AdamW([p], lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=wd, foreach=False,
+                            fused=False)
+    for t in range(1, 11):
+        g16 = to16_host((rng.standard_normal(n) * 1e-3).astype(np.float32), "bf16")
+        g = oracle.to_f32(g16, "bf16")
+        oracle.adam_step(L, 0, "bf16", 0, n, master, m, v, g16, shard, np.float32(1.0), False,
+                         oracle.AdamHParams(weight_decay=wd, step=t))
+        p.grad = torch.from_numpy(g.copy())
+        opt.step()
+    tw = p.detach().numpy()
+    assert np.max(np.abs(master.astype(np.float64) - tw)) <= 10 * (2e-6 * 1e-3) + 6 * np.max(_ulp32(w0))
+    # the decay is visible: it moved the weights by about 10 * lr * wd * |w0|
+    plain = w0.copy()
+    m2, v2 = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    rng = np.random.default_rng(4)
+    rng.standard_normal(n)
+    for t in range(1, 11):
+        g16 = to16_host((rng.standard_normal(n) * 1e-3).astype(np.float32), "bf16")
+        oracle.adam_step(L, 0, "bf16", 0, n, plain, m2, v2, g16, shard.copy(), np.float32(1.0), False,
+                         oracle.AdamHParams(step=t))
+    shrink = np.abs(plain.astype(np.float64) - master)
+    big = np.abs(w0) > 0.01
+    assert np.all(shrink[big] >= 0.5 * 10 * 1e-3 * wd * np.abs(w0[big]))
 
 
 def test_nonfinite_skips_step_and_padding_stays_zero():
