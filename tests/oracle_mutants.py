@@ -305,3 +305,136 @@ def install(name: str) -> None:
     if name not in MUTANTS:
         raise KeyError(f"unknown oracle mutant {name!r}")
     MUTANTS[name](name)
+
+
+# ---- the coordinator (oracle/coordinator.py) -------------------------------
+
+import oracle.coordinator as oc  # noqa: E402
+
+
+def _fetch_with(slip):
+    def fetch(self, m):
+        k = self.step_pos
+        self.step_pos += 1
+        self.fetched_at[m] = k
+        if self.mode == oc.RECORD:
+            self.trace.append(m)
+        elif self.mode == oc.COMPLETE and slip != "no_order_check" and (k >= len(self.trace) or self.trace[k] != m):
+            self._invalidate()
+        ops = []
+        need = [d for d in self._partitioned(m) if self.status[d] == oc.NOT_AVAILABLE]
+        for d in need:
+            self.status[d] = oc.INFLIGHT
+            self.live += self.numel[d]
+        if need:
+            ops.append((oc.CURRENT, sorted(need)))
+        for d in self._partitioned(m):
+            self.status[d] = oc.AVAILABLE
+        if self.mode == oc.COMPLETE and self.cfg.prefetch_bucket_size > 0:
+            while self.cursor < len(self.script) and self.script[self.cursor][0] <= k:
+                self.cursor += 1
+            bucket, filled = [], 0
+            while self.cursor < len(self.script):
+                pos, d = self.script[self.cursor]
+                if self.status[d] != oc.NOT_AVAILABLE:
+                    if slip != "no_marks":
+                        self.marked[d] = max(self.marked.get(d, -1), pos)
+                    self.cursor += 1
+                    continue
+                n = self.numel[d]
+                if slip == "bucket_overfill":
+                    if bucket and filled > self.cfg.prefetch_bucket_size:
+                        break
+                elif bucket and filled + n > self.cfg.prefetch_bucket_size:
+                    break
+                if slip == "live_limit_ge":
+                    if self.live + n >= self.cfg.max_live_parameters:
+                        break
+                elif self.live + n > self.cfg.max_live_parameters:
+                    break
+                bucket.append(d)
+                filled += n
+                self.live += n
+                self.status[d] = oc.INFLIGHT
+                self.marked[d] = max(self.marked.get(d, -1), pos)
+                self.cursor += 1
+            if bucket:
+                ops.append((oc.PREFETCH, sorted(bucket)))
+        return ops
+    return fetch
+
+
+def _reused_soon_inclusive(self, d, k):
+    """The using module's own size counted into the distance."""
+    dist = 0
+    for k2 in range(k + 1, len(self.trace)):
+        m2 = self.trace[k2]
+        dist += self._size(m2)
+        if d in self.modules[m2]:
+            return dist <= self.cfg.max_reuse_distance
+        if dist > self.cfg.max_reuse_distance:
+            return False
+    return False
+
+
+def _release_ignoring_reuse(orig):
+    def release(self, m):
+        saved = self.mode
+        self.mode = oc.RECORD if self.mode == oc.COMPLETE else self.mode   # skips the reuse test
+        try:
+            return orig(self, m)
+        finally:
+            self.mode = saved
+    return release
+
+
+def _release_ignoring_marks(orig):
+    def release(self, m):
+        """A parameter the prefetcher marked for a later use is released anyway."""
+        saved = self.marked
+        self.marked = {}
+        try:
+            return orig(self, m)
+        finally:
+            self.marked = saved
+    return release
+
+
+def _reset_step_records_forever(self):
+    """The recording step never completes the trace."""
+    if self.mode == oc.INVALID or self.mode == oc.RECORD:
+        self.mode = oc.RECORD
+        self.trace = []
+        self.script = []
+    self.step_pos = 0
+    self.cursor = 0
+    self.marked = {}
+    self.fetched_at = {}
+    return self.mode
+
+
+def _fnv1_bytes(data):
+    """FNV-1 (multiply, then xor) instead of FNV-1a."""
+    h = 14695981039346656037
+    for byte in data:
+        h = (h * 1099511628211) & 0xFFFFFFFFFFFFFFFF
+        h ^= byte
+    return h
+
+
+def _set_coord(attr, fn):
+    setattr(oc.Coordinator, attr, fn)
+
+
+COORD_MUTANTS = {
+    "coord_prefetch_live_limit_off_by_one": lambda n: _set_coord("fetch", _fetch_with("live_limit_ge")),
+    "coord_prefetch_bucket_overfilled": lambda n: _set_coord("fetch", _fetch_with("bucket_overfill")),
+    "coord_prefetch_does_not_mark_live": lambda n: _set_coord("fetch", _fetch_with("no_marks")),
+    "coord_release_ignores_marks": lambda n: _set_coord("release", _release_ignoring_marks(oc.Coordinator.release)),
+    "coord_no_trace_check": lambda n: _set_coord("fetch", _fetch_with("no_order_check")),
+    "coord_reuse_distance_counts_user": lambda n: _set_coord("_reused_soon", _reused_soon_inclusive),
+    "coord_release_ignores_reuse": lambda n: _set_coord("release", _release_ignoring_reuse(oc.Coordinator.release)),
+    "coord_never_completes_trace": lambda n: _set_coord("reset_step", _reset_step_records_forever),
+    "coord_fnv1_not_fnv1a": lambda n: setattr(oc, "fnv1a64_bytes", _fnv1_bytes),
+}
+MUTANTS.update(COORD_MUTANTS)

@@ -1,7 +1,8 @@
 """The oracle's pins bite: each planted mistake in the oracle
 (``oracle_mutants.py``: off-by-ones, dropped terms, swapped constants, wrong
-orders, strides and transposes, on the CPU only) must make the oracle's own
-pin tests fail, and the unmodified oracle must pass them.
+orders, strides and transposes in ``oracle.zero3``; wrong limits, marks,
+distances and hashes in ``oracle.coordinator``; on the CPU only) must make
+the oracle's own pin tests fail, and the unmodified oracle must pass them.
 
 Every run is a separate pytest process over the oracle pin files with
 ``ZS3_ORACLE_MUTANT`` set; hypothesis runs derandomized and without
@@ -16,20 +17,22 @@ from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
-from oracle_mutants import MUTANTS
+from oracle_mutants import COORD_MUTANTS, MUTANTS
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
+COORD_PINS = [os.path.join(HERE, "test_oracle_coordinator.py")]
 PIN_FILES = sorted(f for f in glob.glob(os.path.join(HERE, "test_oracle_*.py"))
-                   if not f.endswith(("test_oracle_mutants.py", "test_oracle_coordinator.py")))
+                   if not f.endswith("test_oracle_mutants.py") and f not in COORD_PINS)
 
 
 def _run(name):
     env = {k: v for k, v in os.environ.items() if k != "ZS3_ORACLE_MUTANT"}
     if name is not None:
         env["ZS3_ORACLE_MUTANT"] = name
+    files = COORD_PINS if name in COORD_MUTANTS else PIN_FILES + (COORD_PINS if name is None else [])
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-m", "not gpu", "-p", "no:cacheprovider",
-                        *PIN_FILES], cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
+                        *files], cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
     return name, r.returncode, (r.stdout + r.stderr)[-1500:]
 
 
