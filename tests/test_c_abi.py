@@ -1,0 +1,33 @@
+"""The C ABI from C: ``include/zs3.h`` compiles as C99 (and as C++17) with
+warnings as errors, links against libzs3.so, and a plain C caller of the
+host-only entry points (layout, bucket and sub-group planning, the
+coordinator, error reporting) gets the toy model's values.  No GPU needed."""
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+PKG = os.path.join(ROOT, "zero_sharded_state_amd")
+LIB = os.path.join(PKG, "libzs3.so")
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="no gcc")
+@pytest.mark.parametrize("lang", ["c99", "c++17"])
+def test_c_caller_of_the_host_entry_points(tmp_path, lang):
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} is not built")
+    exe = str(tmp_path / "c_abi_host")
+    if lang == "c99":
+        cmd = ["gcc", "-std=c99", "-pedantic"]
+    else:
+        cmd = ["g++", "-std=c++17", "-x", "c++"]
+    cmd += ["-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"), os.path.join(HERE, "c_abi_host.c")]
+    cmd += ["-x", "none", "-L", PKG, "-lzs3", f"-Wl,-rpath,{PKG}", "-o", exe]
+    b = subprocess.run(cmd, capture_output=True, text=True)
+    assert b.returncode == 0, b.stdout + b.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
