@@ -1,7 +1,10 @@
 """The C ABI from C: ``include/zs3.h`` compiles as C99 (and as C++17) with
 warnings as errors, links against libzs3.so, and a plain C caller of the
 host-only entry points (layout, bucket and sub-group planning, the
-coordinator, error reporting) gets the toy model's values.  No GPU needed."""
+coordinator, error reporting) gets the toy model's values (no GPU needed).
+On a GPU, a C caller with hipMalloc'd buffers and no Python in the process
+runs partition, gather and reduce-scatter and checks them against their
+definitions."""
 
 import os
 import shutil
@@ -30,4 +33,22 @@ def test_c_caller_of_the_host_entry_points(tmp_path, lang):
     b = subprocess.run(cmd, capture_output=True, text=True)
     assert b.returncode == 0, b.stdout + b.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="no gcc")
+def test_c_caller_of_the_device_entry_points(tmp_path):
+    from gpu_util import note, require_gpu
+    require_gpu()
+    exe = str(tmp_path / "c_abi_device")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"),
+           os.path.join(HERE, "c_abi_device.c"), "-L", PKG, "-lzs3", f"-Wl,-rpath,{PKG}",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-o", exe]
+    b = subprocess.run(cmd, capture_output=True, text=True)
+    assert b.returncode == 0, b.stdout + b.stderr
+    note("c_abi_device: partition, gather, reduce-scatter from C")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
