@@ -141,6 +141,8 @@ ZS3_API zs3_status zs3_layout_info(zs3_layout_t layout, int32_t* world_size, int
 /* bytes_per_rank = 16 * shard_numel: 16-bit param + 16-bit grad + fp32
  * master, momentum, variance per held element ([codex] section 1, 16 Psi/N;
  * [llmnex] section 1, 2 + 2 + 12 bytes). */
+/* The same two totals alone (either output may be NULL). */
+ZS3_API zs3_status zs3_layout_totals(zs3_layout_t layout, int64_t* shard_numel, int64_t* bytes_per_rank);
 
 /* The index-th parameter in ascending ds_id order (0 <= index < n_params). */
 ZS3_API zs3_status zs3_layout_param_at(zs3_layout_t layout, int32_t index, int64_t* ds_id, int64_t* numel,

@@ -35,6 +35,9 @@ int main(void) {
     CHECK(zs3_layout_info(L, &world, &threshold, &n_params, &shard, &bytes) == ZS3_OK);
     CHECK(world == 4 && threshold == 0 && n_params == 4);
     CHECK(shard == 652 && bytes == 16 * 652);            /* 16 Psi / N with Psi = 2,608 */
+    shard = bytes = 0;
+    CHECK(zs3_layout_totals(L, &shard, &bytes) == ZS3_OK && shard == 652 && bytes == 10432);
+    CHECK(zs3_layout_totals(NULL, &shard, &bytes) == ZS3_EINVAL);
     CHECK(zs3_layout_param(L, 2, &nm, &ps, &pers, &off) == ZS3_OK);
     CHECK(nm == 512 && ps == 128 && pers == 0 && off == 512 + 8);
     CHECK(zs3_layout_own_range(L, 0, 3, &lo, &hi) == ZS3_OK && lo == 1536 && hi == 2048);

@@ -28,7 +28,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     syms = _declared_symbols()
-    assert len(syms) == 31
+    assert len(syms) == 32
     assert sorted(zs.EXPORTS) == syms
     for s in syms:
         assert hasattr(L, s), s
@@ -52,6 +52,7 @@ def _assert_same_layout(h, ol):
     assert info["n_params"] == len(ol.params)
     assert info["shard_numel"] == ol.shard_numel
     assert info["bytes_per_rank"] == ol.bytes_per_rank
+    assert zs.zs3_layout_totals(h) == (ol.shard_numel, ol.bytes_per_rank)
     for i, p in enumerate(ol.params):
         q = zs.zs3_layout_param_at(h, i)
         assert (q["ds_id"], q["numel"], q["partition_size"], q["persistent"], q["shard_offset"]) == \

@@ -43,7 +43,7 @@ DTYPES = {"fp16": ZS3_FP16, "bf16": ZS3_BF16}
 # Every exported symbol of include/zs3.h.
 EXPORTS = (
     "zs3_abi_version", "zs3_status_str", "zs3_last_error", "zs3_time_next_launch",
-    "zs3_layout_create", "zs3_layout_destroy", "zs3_layout_info", "zs3_layout_param_at",
+    "zs3_layout_create", "zs3_layout_destroy", "zs3_layout_info", "zs3_layout_totals", "zs3_layout_param_at",
     "zs3_layout_param", "zs3_layout_own_range", "zs3_plan_buckets", "zs3_sub_groups",
     "zs3_bucket_sizes", "zs3_partition", "zs3_gather_coalesced", "zs3_reduce_scatter_local",
     "zs3_layout_norm_slots", "zs3_reduce_scatter_coalesced", "zs3_grad_norm", "zs3_grad_norm_partials",
@@ -95,6 +95,7 @@ _SIGNATURES = {
     "zs3_layout_create": (_c_i32, [_c_i32, _c_i64, _c_i32, _p_i64, _p_i64, ctypes.POINTER(_c_p)]),
     "zs3_layout_destroy": (None, [_c_p]),
     "zs3_layout_info": (_c_i32, [_c_p, _p_i32, _p_i64, _p_i32, _p_i64, _p_i64]),
+    "zs3_layout_totals": (_c_i32, [_c_p, _p_i64, _p_i64]),
     "zs3_layout_param_at": (_c_i32, [_c_p, _c_i32, _p_i64, _p_i64, _p_i64, _p_i32, _p_i64]),
     "zs3_layout_param": (_c_i32, [_c_p, _c_i64, _p_i64, _p_i64, _p_i32, _p_i64]),
     "zs3_layout_own_range": (_c_i32, [_c_p, _c_i64, _c_i32, _p_i64, _p_i64]),
@@ -232,6 +233,13 @@ def zs3_layout_info(layout: int) -> dict:
                                  ctypes.byref(s), ctypes.byref(b)))
     return {"world_size": w.value, "persistence_threshold": t.value, "n_params": np_.value,
             "shard_numel": s.value, "bytes_per_rank": b.value}
+
+
+def zs3_layout_totals(layout: int) -> Tuple[int, int]:
+    """(shard_numel, bytes_per_rank)."""
+    s, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().zs3_layout_totals(layout, ctypes.byref(s), ctypes.byref(b)))
+    return s.value, b.value
 
 
 def zs3_layout_param_at(layout: int, index: int) -> dict:

@@ -624,6 +624,10 @@ zs3_status zs3_layout_info(zs3_layout_t L, int32_t* world_size, int64_t* thresho
     return ok();
 }
 
+zs3_status zs3_layout_totals(zs3_layout_t L, int64_t* shard_numel, int64_t* bytes_per_rank) {
+    return zs3_layout_info(L, nullptr, nullptr, nullptr, shard_numel, bytes_per_rank);
+}
+
 static void put_slot(const Slot& s, int64_t* numel, int64_t* ps, int32_t* persistent, int64_t* offset) {
     if (numel) *numel = s.numel;
     if (ps) *ps = s.ps;
