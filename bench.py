@@ -270,19 +270,18 @@ def cpu_baseline(step, cfg, layers: int):
 
 
 def coordinator_cost(step, cfg, steps: int = 5):
-    """Host cost of the fetch/release coordinator on the workload's module
-    order: the library's (through ctypes, preallocated arguments) and the
-    oracle's, per fetch or release call, on a complete trace."""
+    """Host cost of the library's fetch/release coordinator on the
+    workload's module order, per fetch or release call on a complete trace
+    (through ctypes, preallocated arguments)."""
     import ctypes
 
     import zero_sharded_state_amd as zs
-    from oracle import coordinator as co
     from synth.modules import module_table, step_order
 
     _, mods = module_table(cfg)
     order = step_order(cfg)
-    cc = co.CoordConfig(cfg.prefetch_bucket_size, int(1e9), int(1e9))
-    c = zs.zs3_coord_create(step.h, mods, cc.__dict__)
+    c = zs.zs3_coord_create(step.h, mods, {"prefetch_bucket_size": cfg.prefetch_bucket_size,
+                                           "max_live_parameters": int(1e9), "max_reuse_distance": int(1e9)})
     lib = zs.lib()
     cap = sum(len(m) for m in mods)
     ids = (ctypes.c_int64 * cap)()
@@ -302,7 +301,19 @@ def coordinator_cost(step, cfg, steps: int = 5):
         native_step()
     native = (time.perf_counter() - t0) / (steps * 2 * len(order)) * 1e6
     zs.zs3_coord_destroy(c)
+    return {"calls_per_step": 2 * len(order), "us_per_call_library": round(native, 2),
+            "note": "library timed through ctypes with preallocated arguments (includes the call overhead)"}
 
+
+def cpu_baseline_coordinator(cfg):
+    """CPU-baseline leg: the coordinator oracle on the same module order,
+    per fetch or release call on a complete trace."""
+    from oracle import coordinator as co
+    from synth.modules import module_table, step_order
+
+    _, mods = module_table(cfg)
+    order = step_order(cfg)
+    cc = co.CoordConfig(cfg.prefetch_bucket_size, int(1e9), int(1e9))
     o = co.Coordinator({d: p.numel for d, p in enumerate(cfg.params)},
                        {d: p.numel < cfg.threshold for d, p in enumerate(cfg.params)}, mods, cc)
 
@@ -317,10 +328,7 @@ def coordinator_cost(step, cfg, steps: int = 5):
         oracle_step()
     t0 = time.perf_counter()
     oracle_step()
-    orc = (time.perf_counter() - t0) / (2 * len(order)) * 1e6
-    return {"calls_per_step": 2 * len(order), "us_per_call_library": round(native, 2),
-            "us_per_call_oracle": round(orc, 2),
-            "note": "library timed through ctypes with preallocated arguments (includes the call overhead)"}
+    return round((time.perf_counter() - t0) / (2 * len(order)) * 1e6, 2)
 
 
 # --------------------------------------------------------------------------
@@ -468,6 +476,8 @@ def main():
     if not args.no_cpu_baseline:
         log("running the CPU oracle on its sample")
         cpu = cpu_baseline(step, cfg, args.cpu_layers)
+        if trace is not None:
+            cpu["coordinator_us_per_call"] = cpu_baseline_coordinator(cfg)
 
     line = {
         "metric": METRIC,
