@@ -1,0 +1,138 @@
+// Seeded random exercise of the zs3 host entry points (layout, queries,
+// bucket and sub-group planning, the coordinator, argument errors), for
+// AddressSanitizer / UBSan builds of the host code.  No device calls.
+// Built and run by tests/test_host_sanitizers.py; prints "ok".
+#include <cstdint>
+#include <cstdio>
+#include <vector>
+
+#include "zs3.h"
+
+namespace {
+
+uint64_t g_state = 0x9E3779B97F4A7C15ull;
+uint64_t next() {  // splitmix64
+    uint64_t z = (g_state += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+int64_t uniform(int64_t lo, int64_t hi) { return lo + static_cast<int64_t>(next() % static_cast<uint64_t>(hi - lo + 1)); }
+
+int failures = 0;
+void check(bool ok, const char* what, int iter) {
+    if (!ok) {
+        std::printf("iteration %d: %s\n", iter, what);
+        ++failures;
+    }
+}
+
+}  // namespace
+
+int main() {
+    for (int it = 0; it < 400; ++it) {
+        const int32_t N = static_cast<int32_t>(uniform(1, 70));
+        const int32_t n = static_cast<int32_t>(uniform(0, 40));
+        const int64_t T = uniform(0, 3) == 0 ? 0 : uniform(0, 5000);
+        std::vector<int64_t> ids(n), numel(n);
+        for (int32_t i = 0; i < n; ++i) {
+            ids[i] = 3 * i + uniform(0, 2);
+            numel[i] = uniform(0, 4) == 0 ? uniform(1, 20) : uniform(1, 200000);
+        }
+        for (int32_t i = n - 1; i > 0; --i) std::swap(ids[i], ids[uniform(0, i)]);
+        zs3_layout_t L = nullptr;
+        check(zs3_layout_create(N, T, n, ids.data(), numel.data(), &L) == ZS3_OK, "create", it);
+        if (L == nullptr) continue;
+        int64_t shard = 0, bytes = 0, sum = 0;
+        check(zs3_layout_totals(L, &shard, &bytes) == ZS3_OK && bytes == 16 * shard, "totals", it);
+        for (int32_t i = 0; i < n; ++i) {
+            int64_t d = 0, nm = 0, ps = 0, off = 0, lo = 0, hi = 0;
+            int32_t pers = 0;
+            check(zs3_layout_param_at(L, i, &d, &nm, &ps, &pers, &off) == ZS3_OK && off == sum, "param_at", it);
+            sum += ps;
+            const int32_t r = static_cast<int32_t>(uniform(0, N - 1));
+            check(zs3_layout_own_range(L, d, r, &lo, &hi) == ZS3_OK && lo <= hi && (hi <= nm || hi == lo), "own_range", it);
+        }
+        check(sum == shard, "shard sum", it);
+        // planning with a too-small capacity, then the right one
+        for (int32_t kind : {ZS3_GATHER_BUCKETS, ZS3_REDUCE_BUCKETS}) {
+            const int64_t limit = uniform(1, 400000);
+            int32_t nb = 0;
+            std::vector<int32_t> starts(1);
+            std::vector<int64_t> out(n + 1);
+            zs3_status s = zs3_plan_buckets(L, kind, limit, 0, &nb, starts.data(), out.data());
+            if (s == ZS3_EINVAL) {
+                starts.assign(nb + 1, 0);
+                s = zs3_plan_buckets(L, kind, limit, nb + 1, &nb, starts.data(), out.data());
+            }
+            check(s == ZS3_OK, "plan_buckets", it);
+            if (s == ZS3_OK && nb > 0 && kind == ZS3_GATHER_BUCKETS) {
+                int64_t chunk = 0, full = 0;
+                check(zs3_bucket_sizes(L, starts[1] - starts[0], out.data(), &chunk, &full) == ZS3_OK, "sizes", it);
+            }
+        }
+        {
+            int32_t ng = 0;
+            std::vector<int64_t> be(2);
+            zs3_status s = zs3_sub_groups(L, uniform(1, 300000), 0, &ng, be.data());
+            if (s == ZS3_EINVAL && ng > 0) {
+                be.assign(2 * ng, 0);
+                s = zs3_sub_groups(L, uniform(1, 300000), ng, &ng, be.data());
+            }
+        }
+        // coordinator over random modules (parameters may repeat across modules)
+        if (n > 0) {
+            const int32_t nm = static_cast<int32_t>(uniform(1, 12));
+            std::vector<int32_t> mstart(nm + 1, 0);
+            std::vector<int64_t> mids;
+            for (int32_t m = 0; m < nm; ++m) {
+                const int32_t k = static_cast<int32_t>(uniform(0, 4));
+                std::vector<int64_t> pick;
+                for (int32_t j = 0; j < k; ++j) {
+                    const int64_t d = ids[uniform(0, n - 1)];
+                    bool dup = false;
+                    for (int64_t x : pick) dup |= x == d;
+                    if (!dup) pick.push_back(d);
+                }
+                for (int64_t d : pick) mids.push_back(d);
+                mstart[m + 1] = static_cast<int32_t>(mids.size());
+            }
+            zs3_coord_config cfg;
+            cfg.prefetch_bucket_size = uniform(0, 300000);
+            cfg.max_live_parameters = uniform(1, 1000000);
+            cfg.max_reuse_distance = uniform(0, 500000);
+            zs3_coord_t C = nullptr;
+            check(zs3_coord_create(L, nm, mstart.data(), mids.data(), &cfg, &C) == ZS3_OK, "coord_create", it);
+            if (C != nullptr) {
+                std::vector<int64_t> buf(mids.size() + n + 1);
+                int32_t kinds[2], gst[3], cnt = 0, mode = 0;
+                for (int step = 0; step < 4; ++step) {
+                    const int32_t len = static_cast<int32_t>(uniform(1, 2 * nm));
+                    for (int32_t j = 0; j < len; ++j) {
+                        const int32_t m = step < 3 ? (j % nm) : static_cast<int32_t>(uniform(0, nm - 1));
+                        if (zs3_coord_fetch(C, m, &cnt, kinds, gst, buf.data()) == ZS3_OK)
+                            (void)zs3_coord_release(C, m, &cnt, buf.data());
+                    }
+                    (void)zs3_coord_release_all(C, &cnt, buf.data());
+                    check(zs3_coord_reset_step(C, &mode) == ZS3_OK, "reset", it);
+                }
+                uint64_t a = 0, b = 0;
+                int32_t f = 0;
+                (void)zs3_coord_trace_signature(C, &a, &b, &f);
+                check(zs3_coord_fetch(C, nm, &cnt, kinds, gst, buf.data()) == ZS3_EINVAL, "bad module", it);
+                zs3_coord_destroy(C);
+            }
+        }
+        // argument errors
+        check(zs3_layout_param(L, -7, nullptr, nullptr, nullptr, nullptr) == ZS3_ENOTFOUND, "not found", it);
+        check(zs3_layout_own_range(L, n > 0 ? ids[0] : 0, N, nullptr, nullptr) != ZS3_OK, "bad rank", it);
+        zs3_layout_destroy(L);
+    }
+    {
+        const int64_t d[2] = {1, 1}, m[2] = {5, 5};
+        zs3_layout_t L = nullptr;
+        check(zs3_layout_create(2, 0, 2, d, m, &L) == ZS3_EDUPID && L == nullptr, "dup", -1);
+    }
+    if (failures == 0) std::printf("ok\n");
+    return failures == 0 ? 0 : 1;
+}
