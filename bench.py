@@ -72,6 +72,12 @@ def parse():
     ap.add_argument("--schedule", default="static", choices=("static", "trace"),
                     help="parameter gathers: static gather buckets twice (default), or the buckets the "
                          "trace-driven fetch/release coordinator returns over the forward+backward module order")
+    ap.add_argument("--prefetch-bucket-size", type=float, default=None,
+                    help="gather bucket limit in full elements (default: the workload's); larger than the "
+                         "model puts every parameter in one bucket: one launch per gather pass")
+    ap.add_argument("--reduce-bucket-size", type=float, default=None,
+                    help="gradient bucket limit in full elements (default: the workload's); larger than the "
+                         "model makes the gradient phase one launch")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -347,6 +353,12 @@ def main():
         raise RuntimeError("bench.py needs a GPU")
     torch.cuda.set_device(0)
     cfg = get_config(args.config)
+    if args.prefetch_bucket_size is not None or args.reduce_bucket_size is not None:
+        import dataclasses
+        cfg = dataclasses.replace(
+            cfg,
+            prefetch_bucket_size=int(args.prefetch_bucket_size or cfg.prefetch_bucket_size),
+            reduce_bucket_size=int(args.reduce_bucket_size or cfg.reduce_bucket_size))
     rank = cfg.bench_rank if args.rank is None else args.rank
     log(f"config {cfg.name}: {cfg.title}, rank {rank}")
     step = make_step(cfg, rank, args.rs_streams, args.gather_streams, bool(args.fuse_norm), args.reduce_path,
