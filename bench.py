@@ -150,6 +150,16 @@ class KernelTimer:
             self.hip.hipEventDestroy(self.ct.c_void_p(b))
 
 
+def with_bucket_sizes(cfg, prefetch=None, reduce=None):
+    """The workload with its gather and/or gradient bucket limits replaced
+    (None keeps the workload's)."""
+    if prefetch is None and reduce is None:
+        return cfg
+    import dataclasses
+    return dataclasses.replace(cfg, prefetch_bucket_size=int(prefetch or cfg.prefetch_bucket_size),
+                               reduce_bucket_size=int(reduce or cfg.reduce_bucket_size))
+
+
 def make_step(cfg, rank, rs_streams=1, gather_streams=1, fuse_norm=False, reduce_path="contiguous", offload=False,
               offload_chunk=0):
     from zero_sharded_state_amd.shard_step import AdamConfig, ShardStep
@@ -352,13 +362,7 @@ def main():
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
     torch.cuda.set_device(0)
-    cfg = get_config(args.config)
-    if args.prefetch_bucket_size is not None or args.reduce_bucket_size is not None:
-        import dataclasses
-        cfg = dataclasses.replace(
-            cfg,
-            prefetch_bucket_size=int(args.prefetch_bucket_size or cfg.prefetch_bucket_size),
-            reduce_bucket_size=int(args.reduce_bucket_size or cfg.reduce_bucket_size))
+    cfg = with_bucket_sizes(get_config(args.config), args.prefetch_bucket_size, args.reduce_bucket_size)
     rank = cfg.bench_rank if args.rank is None else args.rank
     log(f"config {cfg.name}: {cfg.title}, rank {rank}")
     step = make_step(cfg, rank, args.rs_streams, args.gather_streams, bool(args.fuse_norm), args.reduce_path,
