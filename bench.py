@@ -469,12 +469,20 @@ def main():
                 "streams": step.gather_streams}
 
     if args.calibrate_copy_gib > 0:
+        # a plain device copy three times with torch (the runtime's copy
+        # kernel), then three times through the library's copy path (a
+        # one-parameter, one-rank partition: k_copy_inline<1>)
+        import zero_sharded_state_amd as zs
         n = int(args.calibrate_copy_gib * 2**30) // 2
         a = torch.empty(n, dtype=torch.int16, device="cuda")
         b = torch.empty_like(a)
         for _ in range(3):
             b.copy_(a)
+        hc = zs.zs3_layout_create(1, 0, [0], [n])
+        for _ in range(3):
+            zs.zs3_partition(hc, 0, cfg.dtype, [0], [a], b)
         torch.cuda.synchronize()
+        zs.zs3_layout_destroy(hc)
         del a, b
 
     coord = None
