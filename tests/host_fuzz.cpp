@@ -1,16 +1,23 @@
 // Seeded random exercise of the zs3 host entry points (layout, queries,
 // bucket and sub-group planning, the coordinator, argument errors), for
-// AddressSanitizer / UBSan builds of the host code.  No device calls.
-// Built and run by tests/test_host_sanitizers.py; prints "ok".
+// AddressSanitizer / UBSan / ThreadSanitizer builds of the host code.  No
+// device calls.  Runs once on the main thread, then on four threads at once,
+// each with its own seed and its own layouts (the library keeps no shared
+// state; the last error is per thread).  Built and run by
+// tests/test_host_sanitizers.py; prints "ok".
+#include <atomic>
 #include <cstdint>
 #include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
 #include <vector>
 
 #include "zs3.h"
 
 namespace {
 
-uint64_t g_state = 0x9E3779B97F4A7C15ull;
+thread_local uint64_t g_state = 0x9E3779B97F4A7C15ull;
 uint64_t next() {  // splitmix64
     uint64_t z = (g_state += 0x9E3779B97F4A7C15ull);
     z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
@@ -19,7 +26,7 @@ uint64_t next() {  // splitmix64
 }
 int64_t uniform(int64_t lo, int64_t hi) { return lo + static_cast<int64_t>(next() % static_cast<uint64_t>(hi - lo + 1)); }
 
-int failures = 0;
+std::atomic<int> failures{0};
 void check(bool ok, const char* what, int iter) {
     if (!ok) {
         std::printf("iteration %d: %s\n", iter, what);
@@ -27,10 +34,9 @@ void check(bool ok, const char* what, int iter) {
     }
 }
 
-}  // namespace
-
-int main() {
-    for (int it = 0; it < 400; ++it) {
+void fuzz(uint64_t seed, int iters) {
+    g_state = seed;
+    for (int it = 0; it < iters; ++it) {
         const int32_t N = static_cast<int32_t>(uniform(1, 70));
         const int32_t n = static_cast<int32_t>(uniform(0, 40));
         const int64_t T = uniform(0, 3) == 0 ? 0 : uniform(0, 5000);
@@ -128,10 +134,36 @@ int main() {
         check(zs3_layout_own_range(L, n > 0 ? ids[0] : 0, N, nullptr, nullptr) != ZS3_OK, "bad rank", it);
         zs3_layout_destroy(L);
     }
+}
+
+}  // namespace
+
+int main() {
+    fuzz(0x9E3779B97F4A7C15ull, 400);
     {
         const int64_t d[2] = {1, 1}, m[2] = {5, 5};
         zs3_layout_t L = nullptr;
         check(zs3_layout_create(2, 0, 2, d, m, &L) == ZS3_EDUPID && L == nullptr, "dup", -1);
+    }
+    // four threads at once; then the last error stays per thread
+    std::vector<std::thread> pool;
+    for (int t = 0; t < 4; ++t) pool.emplace_back(fuzz, 1000003ull * (t + 1), 150);
+    for (auto& th : pool) th.join();
+    {
+        const int64_t d[2] = {1, 1}, m[2] = {5, 5};
+        zs3_layout_t L = nullptr;
+        (void)zs3_layout_create(2, 0, 2, d, m, &L);     // fails on this thread: duplicate ds_id
+        std::string other;
+        std::thread th([&] {
+            const int64_t one = 0, n = 4;
+            zs3_layout_t M = nullptr;
+            (void)zs3_layout_create(1, 0, 1, &one, &n, &M);   // succeeds on another thread
+            other = zs3_last_error();
+            zs3_layout_destroy(M);
+        });
+        th.join();
+        check(std::strlen(zs3_last_error()) > 0, "own thread's error kept", -2);
+        check(other.find("duplicate") == std::string::npos, "error leaked to another thread", -2);
     }
     if (failures == 0) std::printf("ok\n");
     return failures == 0 ? 0 : 1;
