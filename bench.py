@@ -446,7 +446,9 @@ def main():
     for name, ms in phases.items():
         ms /= args.steps
         kernels[name] = {"ms": round(ms, 4), "bytes": phase_bytes[name],
-                         "GBps": round(phase_bytes[name] / (ms * 1e-3) / 1e9, 1) if phase_bytes[name] else None}
+                         "GBps": round(phase_bytes[name] / (ms * 1e-3) / 1e9, 1) if phase_bytes[name] else None,
+                         "hbm_frac": (round(phase_bytes[name] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                                      if phase_bytes[name] else None)}
 
     # Roofline entry of the dominant kernel: the fused gather (pack + unpack
     # of one bucket, k_copy<4>), average duration over the timed launches.
