@@ -1,6 +1,6 @@
 """GPU parity at the workloads' full sizes, in the launch configuration that
 bench.py times (ShardStep: per-bucket calls, fused gathers, gradient buckets
-over four streams).
+over three streams).
 
 * c2 (GPT-2-small set) and c3 (one Llama-3-8B layer): the whole step chained
   for 10 steps on the GPU against the oracle's own 10-step chain from the
@@ -8,8 +8,8 @@ over four streams).
   partials); every output compared.  Variants: the norm fused into the
   reduce, the non-contiguous gradient path (reduce_scatter_coalesced), and
   the optimizer state offloaded to pinned host memory.
-* c4 (Llama-3-8B set, 8.03B parameters, rank 0) and c5 (ragged 7.46B set,
-  N = 64, rank 63, fp16, misaligned), in bench.py's launch configuration
+* c4 (Llama-3-8B set, 8.03B parameters, ranks 0 and 7) and c5 (ragged 7.46B
+  set, N = 64, ranks 63 and 0, fp16, misaligned), in bench.py's launch configuration
   (three gradient streams, fused norm): each call fed fresh synthetic
   inputs, its outputs checked on a sample of whole parameters (the oracle
   recomputes those parameters only) or, for the norm, over the whole flat
@@ -207,13 +207,13 @@ def _sample_params(L, cfg, k=6):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["c4", "c5"])
-def test_fullsize_calls_on_sampled_parameters(name):
+@pytest.mark.parametrize("name,rank", [("c4", 0), ("c4", 7), ("c5", 63), ("c5", 0)])
+def test_fullsize_calls_on_sampled_parameters(name, rank):
     """In bench.py's launch configuration: gradient buckets over three
-    streams, the norm fused into the reduce-scatter."""
+    streams, the norm fused into the reduce-scatter; the first and the last
+    rank of each workload (c5's last rank holds every padded tail)."""
     import torch
     cfg = get_config(name)
-    rank = cfg.bench_rank
     N, dt = cfg.world_size, cfg.dtype
     note(f"fullsize {name} rank={rank}: set-up")
     step = _step(cfg, rank, fuse_norm=True)
