@@ -177,7 +177,7 @@ def fill_inputs(step, cfg):
 
     dev = step.device
     if step.F:
-        device_normal16(step.F, cfg.weight_std, cfg.dtype, dev, (cfg.seed, cfg.config_id, KIND_WEIGHT, 0),
+        device_normal16(step.full.numel(), cfg.weight_std, cfg.dtype, dev, (cfg.seed, cfg.config_id, KIND_WEIGHT, 0),
                         out=step.full)
     if step.P:
         device_normal16(step.P, cfg.weight_std, cfg.dtype, dev, (cfg.seed, cfg.config_id, KIND_WEIGHT, 1),

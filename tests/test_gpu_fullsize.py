@@ -222,7 +222,8 @@ def test_fullsize_calls_on_sampled_parameters(name, rank):
     dev = step.device
     try:
         # ---- partition: synthetic full parameters -> shard
-        device_normal16(step.F, cfg.weight_std, dt, dev, (cfg.seed, cfg.config_id, KIND_WEIGHT, 0), out=step.full)
+        device_normal16(step.full.numel(), cfg.weight_std, dt, dev, (cfg.seed, cfg.config_id, KIND_WEIGHT, 0),
+                        out=step.full)
         device_normal16(step.P, cfg.weight_std, dt, dev, (cfg.seed, cfg.config_id, KIND_WEIGHT, 1), out=step.pers_full)
         note(f"fullsize {name}: partition")
         step.repartition()

@@ -82,11 +82,18 @@ class ShardStep:
         self.sub_groups = zs.zs3_sub_groups(self.h, sub_group_size)
 
         # ---- buffer layout (element offsets) ----
+        # Every bucket's gathered buffer and its all-gather buffer start on a
+        # 16-byte boundary.  A one-parameter bucket's N chunks then sit at the
+        # same byte address modulo 16 as the parts of the parameter they fill
+        # (chunk v at v*partition_size in both), so its unpack is one
+        # co-aligned 128-bit copy even when the sizes are ragged.
         self.full_off: Dict[int, int] = {}     # ds_id -> offset of its gathered view in `full`
         self.bucket_meta: List[Tuple[int, int, int, int]] = []   # (full_off, full_n, wire_off, chunk_n)
         f = w = 0
+        self.F = 0                              # gathered elements (the real ones: sum of numels)
         for b in self.gather_buckets:
             chunk_n, full_n = zs.zs3_bucket_sizes(self.h, b)
+            f, w = -(-f // 8) * 8, -(-w // 8) * 8
             self.bucket_meta.append((f, full_n, w, chunk_n))
             o = f
             for d in b:                         # ds_id order inside a bucket
@@ -94,7 +101,8 @@ class ShardStep:
                 o += self.by_id[d]["numel"]
             f += full_n
             w += self.N * chunk_n
-        self.F, self.W = f, w
+            self.F += full_n
+        self.full_len, self.W = f, w
         self.pers = [p for p in self.params if p["persistent"]]
         self.pers_off = {}
         o = 0
@@ -106,7 +114,7 @@ class ShardStep:
 
         i16, f32 = torch.int16, torch.float32
         dev = self.device
-        self.full = torch.empty(max(1, self.F), dtype=i16, device=dev)        # gathered parameters
+        self.full = torch.empty(max(1, self.full_len), dtype=i16, device=dev)  # gathered parameters
         self.pers_full = torch.empty(max(1, self.P), dtype=i16, device=dev)   # whole persistent params
         self.wire = torch.empty(max(1, self.W), dtype=i16, device=dev)        # per-bucket all-gather output
         self.shard = torch.zeros(max(1, self.S), dtype=i16, device=dev)
