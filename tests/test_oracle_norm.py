@@ -80,6 +80,49 @@ def test_equals_l2_norm_of_dense_averaged_gradient():
     assert 0.015 < norm < 0.04       # N(0, 1e-3) grads averaged over 4 ranks: no clipping
 
 
+@pytest.mark.parametrize("dtype,max_norm,outliers", [("bf16", 1.0, True), ("fp16", 0.01, False),
+                                                      ("bf16", 1.0, False)])
+def test_coefficient_matches_torch_clip_grad_norm(dtype, max_norm, outliers):
+    """[llmnex] pitfall 1 names torch's clip_grad_norm_ as the routine that
+    must see the global norm.  Handed the dense averaged gradient (every
+    element once, persistent parameters once) as fp64 gradients, it finds
+    the same total norm and multiplies every gradient by the same
+    coefficient -- its epsilon and its clamp at 1 included -- as the
+    oracle's shard-aware norm computes from the ranks' slices.  Two cases
+    clip (outliers; a small max_norm), one does not."""
+    import torch
+
+    rng = np.random.default_rng(7)
+    ids, numels = [3, 0, 5, 1], [1000, 37, 333, 4099]
+    L = oracle.make_layout(8, 50, ids, numels)               # ds_id 0 (37 elements) is persistent
+    grads = []
+    for v in range(8):
+        g = {}
+        for d, n in zip(ids, numels):
+            x = rng.normal(0.0, 1e-2, n).astype(np.float32)
+            if outliers:
+                x[rng.random(n) < 0.01] *= 100
+            g[d] = to16_host(x, dtype)
+        grads.append(g)
+    outs = _rs(L, dtype, grads)
+    norm, coef, scale, bad = _norm_all_ranks(L, dtype, outs, max_norm)
+    assert not bad
+    params = []
+    for p in L.params:
+        cat = np.concatenate([o[p.shard_offset:p.shard_offset + p.partition_size] for o in outs])[:p.numel]
+        t = torch.nn.Parameter(torch.zeros(p.numel, dtype=torch.float64))
+        t.grad = torch.from_numpy(oracle.to_f32(cat, dtype).astype(np.float64))
+        params.append(t)
+    before = [t.grad.clone() for t in params]
+    total = torch.nn.utils.clip_grad_norm_(params, max_norm, norm_type=2.0)
+    assert float(total) == pytest.approx(norm, rel=1e-13)
+    applied = torch.cat([(t.grad / b)[b != 0] for t, b in zip(params, before)])
+    assert float(applied.min()) == pytest.approx(coef, rel=1e-13)
+    assert float(applied.max()) == pytest.approx(coef, rel=1e-13)
+    assert (coef < 1.0) == (max_norm < norm)
+    assert scale == np.float32(coef)
+
+
 def test_persistent_counted_once():
     L = oracle.make_layout(4, 10, [0, 1], [3, 40])        # param 0 persistent
     g = {0: to16_host(np.array([1.0, 2.0, 2.0], np.float32), "bf16"),
