@@ -1,0 +1,158 @@
+"""GPU parity on seeded random layouts: each case draws a world size (1 to
+64), a persistence threshold, up to 16 parameters with ragged sizes (mostly
+tiny, some spanning many workgroup pieces), a dtype, a rank, base-pointer
+misalignments and bucket limits, then runs the whole chain through the C
+ABI -- partition, fused gather of every gather bucket (shuffled requests),
+slice-only reduce-scatter of every reduce bucket, the norm (the other
+ranks' partial sums filled in from the oracle), two Adam steps on the
+reduced gradient -- and compares every output with the oracle: bit-exact
+for the 16-bit outputs and the fp32 state, 1e-12 for the norm's sums."""
+
+import numpy as np
+import pytest
+
+import oracle
+import zero_sharded_state_amd as zs
+from synth.gen import random_bits16
+
+from gpu_util import Buf16, Buf32, note, require_gpu, sync
+
+pytestmark = pytest.mark.gpu
+
+WORLD = [1, 2, 3, 4, 5, 7, 8, 13, 16, 31, 64]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _case(seed):
+    rng = np.random.default_rng(10_000 + seed)
+    N = int(rng.choice(WORLD))
+    T = int(rng.choice([0, 10, 100, 1000]))
+    n = int(rng.integers(1, 17))
+    kind = rng.random(n)
+    numels = [int(rng.integers(1, 300)) if k < 0.6 else int(rng.integers(300, 20_000)) if k < 0.9
+              else int(rng.integers(20_000, 120_000)) for k in kind]
+    ids = [int(x) for x in rng.choice(10 * n + 5, n, replace=False)]
+    dtype = "bf16" if rng.random() < 0.5 else "fp16"
+    r = int(rng.integers(0, N))
+    shifts = [int(x) for x in rng.integers(0, 8, 6)]
+    return rng, N, T, ids, numels, dtype, r, shifts
+
+
+@pytest.mark.parametrize("seed", range(200))
+def test_random_layout_chain(seed):
+    import torch
+    rng, N, T, ids, numels, dtype, r, sh = _case(seed)
+    tag = f"random seed={seed} N={N} T={T} params={len(ids)} {dtype} rank={r}"
+    h = zs.zs3_layout_create(N, T, ids, numels)
+    L = oracle.make_layout(N, T, ids, numels)
+    try:
+        S = L.shard_numel
+        full = {d: random_bits16(seed, nm, dtype, 0.02, 1, d) for d, nm in zip(ids, numels)}
+
+        # partition
+        note(f"{tag}: partition")
+        srcs = {d: Buf16(full[d].size, shift=(d + sh[0]) % 8, fill=full[d]) for d in ids}
+        order = [int(x) for x in rng.permutation(ids)]
+        shard = Buf16(S, shift=sh[1], fill=np.full(S, 0x7777, np.uint16))
+        zs.zs3_partition(h, r, dtype, order, [srcs[d].ptr() for d in order], shard.ptr())
+        sync()
+        ref_shard = oracle.partition(L, r, full)
+        assert np.array_equal(shard.host(), ref_shard), "partition"
+        shard.check_guards()
+
+        # fused gather of every gather bucket
+        shards = [oracle.partition(L, v, full) for v in range(N)]
+        limit = int(rng.integers(1, sum(numels) + 2))
+        for bi, bucket in enumerate(oracle.gather_buckets(L, limit)):
+            chunk_n, full_n = oracle.bucket_sizes(L, bucket)
+            ref_chunks = [oracle.pack(L, v, bucket, shards[v]) for v in range(N)]
+            ref_full, ref_offs = oracle.unpack(L, bucket, ref_chunks)
+            req = [int(x) for x in rng.permutation(bucket)]
+            note(f"{tag}: gather bucket {bi} ({len(bucket)} params)")
+            chunks = [Buf16(chunk_n, shift=(sh[2] + v) % 8, fill=ref_chunks[v]) for v in range(N)]
+            own = Buf16(chunk_n, shift=sh[2])
+            fl = Buf16(full_n, shift=sh[3])
+            ptrs = [c.ptr() for c in chunks]
+            ptrs[r] = own.ptr()
+            offs = zs.zs3_gather_coalesced(h, r, dtype, zs.ZS3_PACK | zs.ZS3_UNPACK, req, shard.ptr(), own.ptr(),
+                                           ptrs, fl.ptr())
+            sync()
+            assert np.array_equal(own.host(), ref_chunks[r]), f"packed chunk of bucket {bi}"
+            assert np.array_equal(fl.host(), ref_full), f"gathered bucket {bi}"
+            assert offs == [ref_offs[d] for d in req]
+            own.check_guards()
+            fl.check_guards()
+
+        # slice-only reduce-scatter of every reduce bucket
+        grads = [{d: random_bits16(seed * 97 + v, nm, dtype, 1e-3, 2, d) for d, nm in zip(ids, numels)}
+                 for v in range(N)]
+        rlimit = int(rng.integers(1, sum(numels) + 2))
+        buckets = oracle.reduce_buckets(L, rlimit)
+        ref_grad = np.zeros(S, np.uint16)
+        gflat = Buf16(S, shift=sh[4], fill=np.full(S, 0x3C3C, np.uint16))
+        keep = []
+        for bi, b in enumerate(buckets):
+            oracle.reduce_scatter(L, r, dtype, b, grads, ref_grad)
+            src = []
+            for d in b:
+                lo, hi = L.own_range(L.slot(d), r)
+                for v in range(N):
+                    buf = Buf16(hi - lo, shift=(v + sh[5]) % 8, fill=grads[v][d][lo:hi]) if hi > lo else None
+                    keep.append(buf)
+                    src.append(buf.ptr() if buf is not None else 0)
+            note(f"{tag}: reduce-scatter bucket {bi} ({len(b)} params)")
+            zs.zs3_reduce_scatter_local(h, r, dtype, b, src, gflat.ptr())
+        sync()
+        assert np.array_equal(gflat.host(), ref_grad), "reduce-scatter"
+        gflat.check_guards()
+        del keep
+
+        # norm: the other ranks' partial sums from the oracle, this rank's from the GPU
+        parts = []
+        for v in range(N):
+            gv = ref_grad if v == r else np.zeros(S, np.uint16)
+            if v != r:
+                for b in buckets:
+                    oracle.reduce_scatter(L, v, dtype, b, grads, gv)
+            parts.append(oracle.grad_norm_partial(L, v, dtype, gv))
+        max_norm = float(rng.choice([1e-3, 1.0, 1e3]))
+        norm, coef, scale, bad = oracle.grad_norm_finalize([a for a, _ in parts], parts[0][1], max_norm)
+        sumsq = torch.tensor([a for a, _ in parts] + [0.0], dtype=torch.float64, device="cuda")
+        sumsq[r] = -1.0
+        outs = torch.zeros(2, dtype=torch.float64, device="cuda")
+        note(f"{tag}: norm")
+        zs.zs3_grad_norm(h, r, dtype, gflat.ptr(), sumsq, True, max_norm, 1.0, outs.data_ptr(),
+                         outs.data_ptr() + 8, outs.data_ptr() + 12)
+        sync()
+        s = sumsq.cpu().numpy()
+        assert s[r] == pytest.approx(parts[r][0], rel=1e-12, abs=0)
+        assert s[N] == pytest.approx(parts[0][1], rel=1e-12, abs=0)
+        o = outs.cpu().numpy()
+        assert float(o[0]) == pytest.approx(norm, rel=1e-12, abs=1e-300)
+        assert int(o[1:2].view(np.int32)[1]) == int(bad) == 0
+
+        # two Adam steps on the reduced gradient, with the oracle's scale
+        w, m, v_ = oracle.init_state(ref_shard, dtype)
+        W, M, V = Buf32(S, sh[0], w), Buf32(S, sh[1], m), Buf32(S, sh[2], v_)
+        sub = oracle.sub_groups(L, int(rng.integers(1, S + 2)))
+        scal = torch.tensor([float(scale), 0.0], dtype=torch.float32, device="cuda")
+        out16 = ref_shard.copy()
+        for t in (1, 2):
+            hp = oracle.AdamHParams(1e-3, 0.9, 0.999, 1e-8, 0.0, t)
+            note(f"{tag}: adam step {t} over {len(sub)} sub-groups")
+            for b, e in sub:
+                oracle.adam_step(L, r, dtype, b, e, w, m, v_, ref_grad, out16, scale, False, hp)
+                zs.zs3_adam_step(h, r, dtype, b, e, W.ptr(), M.ptr(), V.ptr(), gflat.ptr(), shard.ptr(),
+                                 scal.data_ptr(), scal.data_ptr() + 4, hp)
+        sync()
+        for name, got, ref in (("master", W.host(), w), ("exp_avg", M.host(), m), ("exp_avg_sq", V.host(), v_)):
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"{name} not bit-exact"
+        assert np.array_equal(shard.host(), out16), "16-bit shard after Adam"
+        for b in (W, M, V, shard):
+            b.check_guards()
+    finally:
+        zs.zs3_layout_destroy(h)
