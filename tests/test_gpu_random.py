@@ -156,3 +156,87 @@ def test_random_layout_chain(seed):
             b.check_guards()
     finally:
         zs.zs3_layout_destroy(h)
+
+
+@pytest.mark.parametrize("seed", range(100))
+def test_random_layout_gradient_paths(seed):
+    """The non-contiguous gradient path on random layouts: for every reduce
+    bucket, the rank packs its own full gradients of the bucket's
+    partitioned parameters into the N-chunk send buffer and reduces the N
+    chunks addressed to it (its own read back from the send buffer, the
+    peers' from the oracle's pack) in one call; persistent parameters take
+    the contiguous call.  Both write the fused norm's partial sums into
+    slots that start as NaN.  The flat gradient equals the oracle's
+    reduce-scatter bit for bit, the norm its shard-aware norm."""
+    import torch
+    rng, N, T, ids, numels, dtype, r, sh = _case(5_000 + seed)
+    tag = f"random paths seed={seed} N={N} T={T} params={len(ids)} {dtype} rank={r}"
+    h = zs.zs3_layout_create(N, T, ids, numels)
+    L = oracle.make_layout(N, T, ids, numels)
+    try:
+        S = L.shard_numel
+        grads = [{d: random_bits16(seed * 89 + v, nm, dtype, 1e-3, 3, d) for d, nm in zip(ids, numels)}
+                 for v in range(N)]
+        n_slots, _ = zs.zs3_layout_norm_slots(h)
+        partials = torch.full((max(1, n_slots),), float("nan"), dtype=torch.float64, device="cuda")
+        out = Buf16(S, shift=sh[0], fill=np.full(S, 0x2B2B, np.uint16))
+        ref = np.zeros(S, np.uint16)
+        buckets = oracle.reduce_buckets(L, int(rng.integers(1, sum(numels) + 2)))
+        keep = []
+        for bi, b in enumerate(buckets):
+            oracle.reduce_scatter(L, r, dtype, b, grads, ref)
+            pb = [int(x) for x in rng.permutation([d for d in b if not L.slot(d).persistent])]
+            qb = [d for d in b if L.slot(d).persistent]
+            if pb:
+                peers = [oracle.scatter_pack(L, pb, grads[v])[r] for v in range(N)]
+                C = peers[0].size
+                own = {d: Buf16(L.slot(d).numel, shift=(d + sh[1]) % 8, fill=grads[r][d]) for d in pb}
+                send = Buf16(N * C, shift=sh[2])
+                bufs = [Buf16(C, shift=(v + sh[3]) % 8, fill=peers[v]) for v in range(N)]
+                keep += [send, *own.values(), *bufs]
+                recv = [x.ptr() for x in bufs]
+                recv[r] = send.ptr() + 2 * r * C
+                note(f"{tag}: bucket {bi} pack+reduce ({len(pb)} params)")
+                zs.zs3_reduce_scatter_coalesced(h, r, dtype, zs.ZS3_PACK | zs.ZS3_REDUCE, pb,
+                                                grads=[own[d].ptr() for d in pb], send=send.ptr(),
+                                                recv_chunks=recv, grad_flat=out.ptr(), partials=partials.data_ptr())
+            if qb:
+                src = []
+                for d in qb:
+                    for v in range(N):
+                        buf = Buf16(L.slot(d).numel, shift=(v + sh[4]) % 8, fill=grads[v][d])
+                        keep.append(buf)
+                        src.append(buf.ptr())
+                note(f"{tag}: bucket {bi} persistent ({len(qb)} params)")
+                zs.zs3_reduce_scatter_local(h, r, dtype, qb, src, out.ptr(), partials=partials.data_ptr())
+        sync()
+        assert np.array_equal(out.host(), ref), "flat gradient"
+        out.check_guards()
+        del keep
+        # the norm from the fused partial sums, the other ranks' sums from the oracle
+        parts = []
+        for v in range(N):
+            gv = ref if v == r else np.zeros(S, np.uint16)
+            if v != r:
+                for b in buckets:
+                    oracle.reduce_scatter(L, v, dtype, b, grads, gv)
+            parts.append(oracle.grad_norm_partial(L, v, dtype, gv))
+        max_norm = float(rng.choice([1e-3, 1.0, 1e3]))
+        norm, coef, scale, bad = oracle.grad_norm_finalize([a for a, _ in parts], parts[0][1], max_norm)
+        sumsq = torch.tensor([a for a, _ in parts] + [-1.0], dtype=torch.float64, device="cuda")
+        sumsq[r] = -1.0
+        outs = torch.zeros(2, dtype=torch.float64, device="cuda")
+        note(f"{tag}: norm from the fused partials")
+        zs.zs3_grad_norm_partials(h, r, partials, sumsq, True, max_norm, 1.0, outs.data_ptr(), outs.data_ptr() + 8,
+                                  outs.data_ptr() + 12)
+        sync()
+        s = sumsq.cpu().numpy()
+        assert s[r] == pytest.approx(parts[r][0], rel=1e-12, abs=0)
+        assert s[N] == pytest.approx(parts[0][1], rel=1e-12, abs=0)
+        o = outs.cpu().numpy()
+        assert float(o[0]) == pytest.approx(norm, rel=1e-12, abs=1e-300)
+        assert int(o[1:2].view(np.int32)[1]) == int(bad) == 0
+        got_scale = float(o[1:2].view(np.float32)[0])
+        assert abs(got_scale - float(scale)) <= float(np.spacing(np.float32(scale)))
+    finally:
+        zs.zs3_layout_destroy(h)
