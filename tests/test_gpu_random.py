@@ -6,7 +6,9 @@ ABI -- partition, fused gather of every gather bucket (shuffled requests),
 slice-only reduce-scatter of every reduce bucket, the norm (the other
 ranks' partial sums filled in from the oracle), two Adam steps on the
 reduced gradient -- and compares every output with the oracle: bit-exact
-for the 16-bit outputs and the fp32 state, 1e-12 for the norm's sums."""
+for the 16-bit outputs and the fp32 state, 1e-12 for the norm's sums.  More
+random layouts take the non-contiguous gradient path with the fused norm,
+and Adam on state held in pinned host memory."""
 
 import numpy as np
 import pytest
@@ -238,5 +240,61 @@ def test_random_layout_gradient_paths(seed):
         assert int(o[1:2].view(np.int32)[1]) == int(bad) == 0
         got_scale = float(o[1:2].view(np.float32)[0])
         assert abs(got_scale - float(scale)) <= float(np.spacing(np.float32(scale)))
+    finally:
+        zs.zs3_layout_destroy(h)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_layout_offloaded_adam(seed):
+    """Adam on fp32 state in pinned host memory (read through the device
+    mapping, or staged through a small device buffer in chunks of a random
+    size) on random layouts and sub-groups: the same bits as the device
+    Adam and the oracle after two steps."""
+    import torch
+    rng, N, T, ids, numels, dtype, r, sh = _case(9_000 + seed)
+    chunk = None if rng.random() < 0.4 else int(rng.integers(8, 70_000))
+    tag = f"random offload seed={seed} N={N} params={len(ids)} {dtype} rank={r} chunk={chunk}"
+    h = zs.zs3_layout_create(N, T, ids, numels)
+    L = oracle.make_layout(N, T, ids, numels)
+    try:
+        S = L.shard_numel
+        pad = oracle.padding_mask(L, r)
+        shard0 = random_bits16(seed, S, dtype, 0.02, 4)
+        shard0[pad] = 0
+        w0, _, _ = oracle.init_state(shard0, dtype)
+        m0 = (rng.standard_normal(S) * 1e-4).astype(np.float32)
+        v0 = (rng.random(S) * 1e-7).astype(np.float32)
+        m0[pad] = 0
+        v0[pad] = 0
+        dw, dm, dv = (Buf32(S, sh[i], x) for i, x in enumerate((w0, m0, v0)))
+        ds = Buf16(S, shift=sh[3], fill=shard0)
+        hw, hm, hv = (torch.from_numpy(x.copy()).pin_memory() for x in (w0, m0, v0))
+        hs = Buf16(S, shift=sh[4], fill=shard0)
+        stage = torch.full((6 * (chunk + 8),), float("nan"), dtype=torch.float32, device="cuda") if chunk else None
+        scale = np.float32(rng.choice([1.0, 0.37]))
+        scal = torch.tensor([float(scale), 0.0], dtype=torch.float32, device="cuda")
+        cin, cout = torch.cuda.Stream(), torch.cuda.Stream()
+        groups = oracle.sub_groups(L, int(rng.integers(1, S + 2)))
+        ow, om, ov, osh = w0.copy(), m0.copy(), v0.copy(), shard0.copy()
+        for t in (1, 2):
+            g = random_bits16(seed * 13 + t, S, dtype, 1e-3, 6)
+            g[pad] = 0
+            gb = Buf16(S, shift=sh[5], fill=g)
+            hp = oracle.AdamHParams(1e-3, 0.9, 0.999, 1e-8, 0.0, t)
+            note(f"{tag}: step {t} over {len(groups)} sub-groups")
+            for b, e in groups:
+                zs.zs3_adam_step(h, r, dtype, b, e, dw.ptr(), dm.ptr(), dv.ptr(), gb.ptr(), ds.ptr(),
+                                 scal.data_ptr(), scal.data_ptr() + 4, hp)
+                zs.zs3_adam_step_offload(h, r, dtype, b, e, hw, hm, hv, stage, stage.numel() if chunk else 0,
+                                         gb.ptr(), hs.ptr(), scal.data_ptr(), scal.data_ptr() + 4, hp,
+                                         copy_in_stream=cin, copy_out_stream=cout)
+                oracle.adam_step(L, r, dtype, b, e, ow, om, ov, g, osh, scale, False, hp)
+            sync()
+        for name, got, dev, ref in (("master", hw, dw, ow), ("exp_avg", hm, dm, om), ("exp_avg_sq", hv, dv, ov)):
+            assert np.array_equal(got.numpy().view(np.uint32), dev.host().view(np.uint32)), f"{name}: offload"
+            assert np.array_equal(got.numpy().view(np.uint32), ref.view(np.uint32)), f"{name}: oracle"
+        assert np.array_equal(hs.host(), ds.host()) and np.array_equal(hs.host(), osh), "16-bit shard"
+        for b in (dw, dm, dv, ds, hs):
+            b.check_guards()
     finally:
         zs.zs3_layout_destroy(h)
