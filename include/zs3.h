@@ -42,9 +42,12 @@
  *     device to go idle and frees them all before it builds its own (the
  *     only case in which a call synchronises).
  *   - Calls on one layout from several host threads must be serialised by
- *     the caller.  zs3_grad_norm and zs3_grad_norm_partials keep
- *     per-layout scratch: two norm calls on one layout that overlap on
- *     different streams race.
+ *     the caller.  zs3_grad_norm and zs3_grad_norm_partials keep device
+ *     scratch in the layout, one per call shape and stream handle: norm
+ *     calls on different streams may overlap, and calls on one stream are
+ *     ordered by it.  (A stream destroyed with norm work still pending must
+ *     not be replaced by a new stream with the same handle before that work
+ *     is done.)
  */
 #ifndef ZS3_H
 #define ZS3_H
@@ -371,6 +374,27 @@ ZS3_API zs3_status zs3_adam_step(zs3_layout_t layout, int32_t rank, int32_t dtyp
                          float* master, float* exp_avg, float* exp_avg_sq, const void* grad_flat,
                          void* shard_flat, const float* scale, const int32_t* nonfinite,
                          const zs3_adam_params* hp, void* stream);
+
+/* ------------------------------------------ (5a) fp32 master partition
+ * [codex] 6.1: when the optimizer is built, each sub-group's fp32 partition
+ * is created from the rank's 16-bit shard, and that fp32 master is what the
+ * optimizer steps.  [llmnex] section 1: the optimizer state per element is
+ * the fp32 master weight, the momentum and the variance; Adam starts both
+ * moments at 0.
+ *
+ * For every position e in [begin, end) of the rank's flat shard:
+ *   master[e] = shard_flat[e] widened exactly to float at real positions,
+ *               0 at padding positions (whatever shard_flat holds there);
+ *   exp_avg[e] = exp_avg_sq[e] = 0 (either pointer may be NULL: not written).
+ * Positions outside [begin, end) are not touched.  shard_flat: dev 16-bit;
+ * master, exp_avg, exp_avg_sq: dev fp32; all are the rank's whole flat
+ * arrays (shard_numel elements, indexed from 0), only [begin, end) of them
+ * is accessed.  0 <= begin <= end <= shard_numel.  The arrays must not
+ * overlap.
+ */
+ZS3_API zs3_status zs3_init_master(zs3_layout_t layout, int32_t rank, int32_t dtype, int64_t begin, int64_t end,
+                           const void* shard_flat, float* master, float* exp_avg, float* exp_avg_sq,
+                           void* stream);
 
 /* -------------------------------- (f4) Adam on optimizer state held on the host
  * [codex] 6.3: with the optimizer state offloaded, the per-sub-group step

@@ -28,7 +28,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     syms = _declared_symbols()
-    assert len(syms) == 32
+    assert len(syms) == 33
     assert sorted(zs.EXPORTS) == syms
     for s in syms:
         assert hasattr(L, s), s
@@ -172,6 +172,16 @@ def test_call_validation_enqueues_nothing():
             (zs.ZS3_EINVAL, lambda: zs.zs3_grad_norm_partials(h, 0, base, base + 1 << 20, True, 0.0, 1.0,
                                                               base + 8192, base + 8200, base + 8204, stream=0)),
             (zs.ZS3_EALIAS, lambda: zs.zs3_grad_norm_partials(h, 0, base, base + 8, False, stream=0)),
+            # the fp32 master partition
+            (zs.ZS3_EINVAL, lambda: zs.zs3_init_master(h, 0, "bf16", 0, S + 1, base, base + (1 << 20), stream=0)),
+            (zs.ZS3_EINVAL, lambda: zs.zs3_init_master(h, 0, "bf16", 5, 4, base, base + (1 << 20), stream=0)),
+            (zs.ZS3_EINVAL, lambda: zs.zs3_init_master(h, 0, "bf16", 0, S, base, base + (1 << 20) + 2, stream=0)),
+            (zs.ZS3_EINVAL, lambda: zs.zs3_init_master(h, 0, "bf16", 0, S, base, None, stream=0)),
+            (zs.ZS3_EDTYPE, lambda: zs.zs3_init_master(h, 0, 3, 0, S, base, base + (1 << 20), stream=0)),
+            (zs.ZS3_EINVAL, lambda: zs.zs3_init_master(h, 4, "bf16", 0, S, base, base + (1 << 20), stream=0)),
+            (zs.ZS3_EALIAS, lambda: zs.zs3_init_master(h, 0, "bf16", 0, S, base, base + 8, stream=0)),
+            (zs.ZS3_EALIAS, lambda: zs.zs3_init_master(h, 0, "bf16", 0, S, base, base + (1 << 20),
+                                                       base + (1 << 20) + 4 * S - 4, stream=0)),
             # offloaded Adam: every check below runs before any HIP call
             (zs.ZS3_EINVAL, lambda: zs.zs3_adam_step_offload(h, 0, "bf16", 0, S, base, base + (1 << 20),
                                                              base + (2 << 20), base + (3 << 20), 95,
@@ -205,6 +215,7 @@ def test_call_validation_enqueues_nothing():
         assert zs.zs3_gather_coalesced(h, 0, "fp16", zs.ZS3_PACK, [], base, base + 4096, stream=0) == []
         zs.zs3_reduce_scatter_coalesced(h, 0, "fp16", zs.ZS3_PACK | zs.ZS3_REDUCE, [], grads=[], send=base,
                                         recv_chunks=[base] * 4, grad_flat=base + 65536, stream=0)
+        zs.zs3_init_master(h, 0, "fp16", 3, 3, base, base + (1 << 20), stream=0)
     finally:
         zs.zs3_layout_destroy(h)
 

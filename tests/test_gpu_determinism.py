@@ -68,7 +68,6 @@ def _run(step, cfg, t_from, t_to, norms):
         step.gather_pass()
         step.gather_pass()
         step.reduce_scatter()
-        step.repartition()
         step.sumsq.copy_(torch.from_numpy(np.append(peers, 0.0)))
         step.grad_norm()
         step.adam_step(t)

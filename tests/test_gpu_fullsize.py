@@ -152,7 +152,6 @@ def test_chained_steps_match_oracle(name, rank, fuse_norm, reduce_path, offload)
             step.gather_pass()
             step.gather_pass()
             step.reduce_scatter()
-            step.repartition()
             step.sumsq.copy_(torch.from_numpy(np.append(peers, 0.0)))
             step.grad_norm()
             step.adam_step(t)

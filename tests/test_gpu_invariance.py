@@ -128,15 +128,13 @@ def test_adam_does_not_depend_on_sub_groups(case):
     try:
         r = 0
         shard0 = oracle.partition(L, r, full)
-        w0, _, _ = oracle.init_state(shard0, "bf16")
         grads = [random_bits16(seed * 13 + t, L.shard_numel, "bf16", 1e-3, 7) for t in range(1, 6)]
         scal = torch.tensor([0.75, 0.0], dtype=torch.float32, device="cuda")
         res = {}
         for label, groups in (("whole shard", [(0, L.shard_numel)]), ("per parameter", oracle.sub_groups(L, 1))):
-            W = Buf32(L.shard_numel, fill=w0)
-            M = Buf32(L.shard_numel, fill=np.zeros_like(w0))
-            V = Buf32(L.shard_numel, fill=np.zeros_like(w0))
+            W, M, V = Buf32(L.shard_numel), Buf32(L.shard_numel), Buf32(L.shard_numel)
             S = Buf16(L.shard_numel, fill=shard0)
+            zs.zs3_init_master(h, r, "bf16", 0, L.shard_numel, S.ptr(), W.ptr(), M.ptr(), V.ptr())
             note(f"invariance adam N={N} {label} groups={len(groups)}")
             for t, g in enumerate(grads, start=1):
                 G = Buf16(L.shard_numel, fill=g)

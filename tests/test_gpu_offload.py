@@ -11,7 +11,7 @@ import oracle
 import zero_sharded_state_amd as zs
 from synth.gen import random_bits16
 
-from gpu_util import Buf16, note, require_gpu, sync
+from gpu_util import Buf16, Buf32, note, require_gpu, sync
 from test_gpu_parity import _layout, _problem
 
 pytestmark = pytest.mark.gpu
@@ -38,7 +38,11 @@ def test_offload_matches_device_adam_and_oracle(seed, N, T, n, mx, chunk):
         rng = np.random.default_rng(seed)
         shard0 = random_bits16(seed, S, "bf16", 0.02, 3)
         shard0[oracle.padding_mask(L, r)] = 0
-        w0, m0, v0 = oracle.init_state(shard0, "bf16")
+        wbuf, sbuf = Buf32(S), Buf16(S, fill=shard0)
+        zs.zs3_init_master(h, r, "bf16", 0, S, sbuf.ptr(), wbuf.ptr())     # the master from the library
+        sync()
+        w0 = wbuf.host()
+        assert np.array_equal(w0.view(np.uint32), oracle.init_state(shard0, "bf16")[0].view(np.uint32))
         m0 = (rng.standard_normal(S) * 1e-4).astype(np.float32)
         v0 = (rng.random(S) * 1e-7).astype(np.float32)
         # device reference: zs3_adam_step on device copies

@@ -333,8 +333,16 @@ def _adam_chain(prob, dtype, shift, wd):
         r = N - 1
         shard = oracle.partition(L, r, full)
         w, m, v = oracle.init_state(shard, dtype)
-        W, M, V = Buf32(L.shard_numel, shift, w), Buf32(L.shard_numel, shift, m), Buf32(L.shard_numel, shift, v)
-        S = Buf16(L.shard_numel, shift, shard)
+        # the GPU side starts from the library's partition and fp32 init
+        srcs = [Buf16(full[d].size, fill=full[d]) for d in ids]
+        S = Buf16(L.shard_numel, shift, np.full(L.shard_numel, 0x7777, np.uint16))
+        zs.zs3_partition(h, r, dtype, ids, [b.ptr() for b in srcs], S.ptr())
+        W, M, V = (Buf32(L.shard_numel, shift, np.full(L.shard_numel, 7.0, np.float32)) for _ in range(3))
+        zs.zs3_init_master(h, r, dtype, 0, L.shard_numel, S.ptr(), W.ptr(), M.ptr(), V.ptr())
+        sync()
+        assert np.array_equal(S.host(), shard), "partition"
+        for name, got, ref in (("master", W.host(), w), ("m", M.host(), m), ("v", V.host(), v)):
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"{name} after init"
         pad = oracle.padding_mask(L, r)
         groups = oracle.sub_groups(L, max(1, L.shard_numel // 3))
         scal = torch.zeros(2, dtype=torch.float32, device="cuda")

@@ -137,9 +137,15 @@ def test_random_layout_chain(seed):
         assert float(o[0]) == pytest.approx(norm, rel=1e-12, abs=1e-300)
         assert int(o[1:2].view(np.int32)[1]) == int(bad) == 0
 
-        # two Adam steps on the reduced gradient, with the oracle's scale
+        # the fp32 state from the library's init of the GPU shard, then two
+        # Adam steps on the reduced gradient with the oracle's scale
         w, m, v_ = oracle.init_state(ref_shard, dtype)
-        W, M, V = Buf32(S, sh[0], w), Buf32(S, sh[1], m), Buf32(S, sh[2], v_)
+        W, M, V = (Buf32(S, sh[i], np.full(S, 7.0, np.float32)) for i in range(3))
+        note(f"{tag}: fp32 master partition")
+        zs.zs3_init_master(h, r, dtype, 0, S, shard.ptr(), W.ptr(), M.ptr(), V.ptr())
+        sync()
+        for name, got, ref in (("master", W.host(), w), ("exp_avg", M.host(), m), ("exp_avg_sq", V.host(), v_)):
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"{name} after init"
         sub = oracle.sub_groups(L, int(rng.integers(1, S + 2)))
         scal = torch.tensor([float(scale), 0.0], dtype=torch.float32, device="cuda")
         out16 = ref_shard.copy()
@@ -261,13 +267,17 @@ def test_random_layout_offloaded_adam(seed):
         pad = oracle.padding_mask(L, r)
         shard0 = random_bits16(seed, S, dtype, 0.02, 4)
         shard0[pad] = 0
-        w0, _, _ = oracle.init_state(shard0, dtype)
         m0 = (rng.standard_normal(S) * 1e-4).astype(np.float32)
         v0 = (rng.random(S) * 1e-7).astype(np.float32)
         m0[pad] = 0
         v0[pad] = 0
-        dw, dm, dv = (Buf32(S, sh[i], x) for i, x in enumerate((w0, m0, v0)))
         ds = Buf16(S, shift=sh[3], fill=shard0)
+        dw = Buf32(S, sh[0], np.full(S, 7.0, np.float32))
+        zs.zs3_init_master(h, r, dtype, 0, S, ds.ptr(), dw.ptr())       # the master from the library
+        sync()
+        w0 = dw.host()
+        assert np.array_equal(w0.view(np.uint32), oracle.init_state(shard0, dtype)[0].view(np.uint32))
+        dm, dv = Buf32(S, sh[1], m0), Buf32(S, sh[2], v0)
         hw, hm, hv = (torch.from_numpy(x.copy()).pin_memory() for x in (w0, m0, v0))
         hs = Buf16(S, shift=sh[4], fill=shard0)
         stage = torch.full((6 * (chunk + 8),), float("nan"), dtype=torch.float32, device="cuda") if chunk else None
@@ -296,5 +306,50 @@ def test_random_layout_offloaded_adam(seed):
         assert np.array_equal(hs.host(), ds.host()) and np.array_equal(hs.host(), osh), "16-bit shard"
         for b in (dw, dm, dv, ds, hs):
             b.check_guards()
+    finally:
+        zs.zs3_layout_destroy(h)
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_layout_init_master(seed):
+    """zs3_init_master ([codex] 6.1: the fp32 partition made from the 16-bit
+    shard) over a random sub-range of a random layout: the exact widening at
+    real positions and 0 at padding (whatever the shard holds there), m and
+    v zero, nothing outside the range or the buffers touched; bit-exact
+    against the oracle's initial state."""
+    rng, N, T, ids, numels, dtype, r, sh = _case(20_000 + seed)
+    h = zs.zs3_layout_create(N, T, ids, numels)
+    L = oracle.make_layout(N, T, ids, numels)
+    try:
+        S = L.shard_numel
+        full = {d: random_bits16(seed, nm, dtype, 0.02, 8, d) for d, nm in zip(ids, numels)}
+        ref_shard = oracle.partition(L, r, full)
+        w, m, v = oracle.init_state(ref_shard, dtype)
+        # the shard as the library's partition writes it, then garbage in its padding
+        shard_in = ref_shard.copy()
+        pad = oracle.padding_mask(L, r)
+        shard_in[pad] = random_bits16(seed + 1, int(pad.sum()), dtype, 1.0, 9) if pad.any() else shard_in[pad]
+        a, b = sorted(int(x) for x in rng.integers(0, S + 1, 2))
+        if rng.random() < 0.3:
+            a, b = 0, S
+        tag = f"init master seed={seed} N={N} params={len(ids)} {dtype} rank={r} range=[{a}, {b}) of {S}"
+        sb = Buf16(S, shift=sh[0], fill=shard_in)
+        fill = np.full(S, 7.0, np.float32)
+        W, M, V = Buf32(S, sh[1], fill), Buf32(S, sh[2], fill), Buf32(S, sh[3], fill)
+        note(tag)
+        zs.zs3_init_master(h, r, dtype, a, b, sb.ptr(), W.ptr(), M.ptr(), V.ptr())
+        sync()
+        for name, got, ref in (("master", W.host(), w), ("exp_avg", M.host(), m), ("exp_avg_sq", V.host(), v)):
+            assert np.array_equal(got[a:b].view(np.uint32), ref[a:b].view(np.uint32)), f"{name} inside the range"
+            assert np.all(got[:a] == 7.0) and np.all(got[b:] == 7.0), f"{name} outside the range"
+        assert np.array_equal(sb.host(), shard_in), "the shard is read only"
+        for buf in (W, M, V, sb):
+            buf.check_guards()
+        # NULL moments: only the master is written
+        W2, M2 = Buf32(S, sh[4], fill), Buf32(S, sh[5], fill)
+        zs.zs3_init_master(h, r, dtype, 0, S, sb.ptr(), W2.ptr(), None, None)
+        sync()
+        assert np.array_equal(W2.host().view(np.uint32), w.view(np.uint32))
+        assert np.all(M2.host() == 7.0)
     finally:
         zs.zs3_layout_destroy(h)

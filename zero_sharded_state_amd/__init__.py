@@ -47,7 +47,8 @@ EXPORTS = (
     "zs3_layout_param", "zs3_layout_own_range", "zs3_plan_buckets", "zs3_sub_groups",
     "zs3_bucket_sizes", "zs3_partition", "zs3_gather_coalesced", "zs3_reduce_scatter_local",
     "zs3_layout_norm_slots", "zs3_reduce_scatter_coalesced", "zs3_grad_norm", "zs3_grad_norm_partials",
-    "zs3_adam_step", "zs3_adam_step_offload", "zs3_coord_create", "zs3_coord_destroy", "zs3_coord_fetch", "zs3_coord_release",
+    "zs3_adam_step", "zs3_adam_step_offload", "zs3_init_master", "zs3_coord_create", "zs3_coord_destroy",
+    "zs3_coord_fetch", "zs3_coord_release",
     "zs3_coord_release_all", "zs3_coord_reset_step", "zs3_coord_info", "zs3_coord_param_status",
     "zs3_coord_trace_signature",
 )
@@ -118,6 +119,7 @@ _SIGNATURES = {
                                _c_p, _c_p, ctypes.POINTER(zs3_adam_params), _c_p]),
     "zs3_adam_step_offload": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                        _c_p, _c_p, _c_p, _c_p, ctypes.POINTER(zs3_adam_params), _c_p, _c_p, _c_p]),
+    "zs3_init_master": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "zs3_coord_create": (_c_i32, [_c_p, _c_i32, _p_i32, _p_i64, ctypes.POINTER(zs3_coord_config),
                                   ctypes.POINTER(_c_p)]),
     "zs3_coord_destroy": (None, [_c_p]),
@@ -363,6 +365,12 @@ def zs3_adam_step_offload(layout: int, rank: int, dtype, begin: int, end: int, h
                                        ctypes.byref(p), _stream(stream),
                                        _stream(copy_in_stream) if copy_in_stream is not None else None,
                                        _stream(copy_out_stream) if copy_out_stream is not None else None))
+
+
+def zs3_init_master(layout: int, rank: int, dtype, begin: int, end: int, shard_flat, master, exp_avg=None,
+                    exp_avg_sq=None, stream=None) -> None:
+    _check(lib().zs3_init_master(layout, rank, _dtype(dtype), int(begin), int(end), _ptr(shard_flat), _ptr(master),
+                                 _ptr(exp_avg), _ptr(exp_avg_sq), _stream(stream)))
 
 
 # ------------------------------------------------------------- coordinator

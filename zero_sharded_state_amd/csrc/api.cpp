@@ -112,7 +112,7 @@ struct Plan {
 
 enum Op : int64_t {
     kOpPartition = 1, kOpPack, kOpUnpack, kOpReduce, kOpNorm, kOpAdam, kOpGather, kOpScatterPack,
-    kOpScatterReduce, kOpNormSlots
+    kOpScatterReduce, kOpNormSlots, kOpInitMaster
 };
 
 constexpr size_t kMaxPlans = 1 << 14;
@@ -1075,7 +1075,10 @@ zs3_status zs3_grad_norm(zs3_layout_t L, int32_t rank, int32_t dtype, const void
     }
     if (overlap(sumsq, 8 * (L->world + 1), grad_flat, 2 * L->shard_numel))
         return fail(ZS3_EALIAS, "sumsq overlaps grad_flat");
-    Key key{{kOpNorm, device_id(), rank, reinterpret_cast<int64_t>(grad_flat)}};
+    // the scratch of the sum-of-squares pass belongs to the plan, and the
+    // plan is keyed by the stream too: norm calls on different streams never
+    // share scratch, and calls on one stream are ordered by it
+    Key key{{kOpNorm, device_id(), rank, reinterpret_cast<int64_t>(grad_flat), reinterpret_cast<int64_t>(stream)}};
     Plan* plan = find_plan(L, key);
     if (plan == nullptr) {
         // real runs: partitioned first, then persistent; adjacent runs merged
@@ -1133,7 +1136,7 @@ zs3_status zs3_grad_norm_partials(zs3_layout_t L, int32_t rank, const double* pa
         if (!(max_norm > 0.0) || !(loss_scale > 0.0)) return fail(ZS3_EINVAL, "max_norm and loss_scale must be > 0");
     }
     if (overlap(sumsq, 8 * (L->world + 1), partials, 8 * L->n_slots)) return fail(ZS3_EALIAS, "sumsq overlaps partials");
-    Key key{{kOpNormSlots, device_id()}};
+    Key key{{kOpNormSlots, device_id(), reinterpret_cast<int64_t>(stream)}};     // scratch per stream, as above
     Plan* plan = find_plan(L, key);
     if (plan == nullptr) {
         Plan np;
@@ -1183,6 +1186,70 @@ zs3_status zs3_adam_step(zs3_layout_t L, int32_t rank, int32_t dtype, int64_t be
 
     return adam_launch(L, rank, dtype, begin, end, master, exp_avg, exp_avg_sq, grad_flat, shard_flat, scale,
                        nonfinite, adam_consts(hp), stream);
+}
+
+// ---------------------------------------------- (5a) fp32 master partition
+
+zs3_status zs3_init_master(zs3_layout_t L, int32_t rank, int32_t dtype, int64_t begin, int64_t end,
+                           const void* shard_flat, float* master, float* exp_avg, float* exp_avg_sq, void* stream) {
+    zs3_status s = check_layout_rank(L, rank);
+    if (s != ZS3_OK) return s;
+    if ((s = check_dtype(dtype)) != ZS3_OK) return s;
+    if (begin < 0 || end < begin || end > L->shard_numel)
+        return fail(ZS3_EINVAL, "range [%lld, %lld) outside [0, %lld]", (long long)begin, (long long)end,
+                    (long long)L->shard_numel);
+    if ((s = check_ptr16(shard_flat, "shard_flat")) != ZS3_OK) return s;
+    if (master == nullptr || !aligned(master, 4)) return fail(ZS3_EINVAL, "master is NULL or not 4-byte aligned");
+    if ((exp_avg != nullptr && !aligned(exp_avg, 4)) || (exp_avg_sq != nullptr && !aligned(exp_avg_sq, 4)))
+        return fail(ZS3_EINVAL, "exp_avg or exp_avg_sq is not 4-byte aligned");
+    const int64_t nb = end - begin;
+    const void* arr[4] = {static_cast<const uint16_t*>(shard_flat) + begin, master + begin,
+                          exp_avg != nullptr ? exp_avg + begin : nullptr,
+                          exp_avg_sq != nullptr ? exp_avg_sq + begin : nullptr};
+    const int64_t bytes[4] = {2 * nb, 4 * nb, 4 * nb, 4 * nb};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (arr[i] != nullptr && arr[j] != nullptr && overlap(arr[i], bytes[i], arr[j], bytes[j]))
+                return fail(ZS3_EALIAS, "init arrays %d and %d overlap", i, j);
+    if (nb == 0) return ok();
+    Key key{{kOpInitMaster, device_id(), rank, begin, end}};
+    Plan* plan = find_plan(L, key);
+    if (plan == nullptr) {
+        // alternating runs of real positions (widened) and padding (zeros)
+        std::vector<std::pair<int64_t, int64_t>> runs;     // (begin, count), real runs tagged below
+        std::vector<int32_t> real;
+        auto add = [&](int64_t a, int64_t b, int32_t is_real) {
+            if (b <= a) return;
+            if (!runs.empty() && real.back() == is_real && runs.back().first + runs.back().second == a) {
+                runs.back().second += b - a;
+                return;
+            }
+            runs.emplace_back(a, b - a);
+            real.push_back(is_real);
+        };
+        for (const Slot& p : L->params) {
+            const int64_t r = p.offset + p.real(rank);
+            add(std::max(begin, p.offset), std::min(end, r), 1);
+            add(std::max(begin, r), std::min(end, p.offset + p.ps), 0);
+        }
+        std::vector<Span> spans;
+        for (size_t i = 0; i < runs.size(); ++i) {
+            const size_t first = spans.size();
+            add_spans(&spans, runs[i].first, runs[i].second, 0, kAdamPiece);
+            for (size_t k = first; k < spans.size(); ++k) spans[k].reserved = real[i];
+        }
+        if ((s = check_grid(static_cast<int64_t>(spans.size()), kAdamSub)) != ZS3_OK) return s;
+        Plan np;
+        np.n_pieces = static_cast<int64_t>(spans.size());
+        std::vector<size_t> offs;
+        if ((s = upload(&np, {{spans.data(), spans.size() * sizeof(Span)}}, 0, &offs)) != ZS3_OK) return s;
+        np.off_pieces = offs[0];
+        store_plan(L, std::move(key), std::move(np), &plan);
+    }
+    return hip_status(launch_init_master(dtype, plan->at<Span>(plan->off_pieces), plan->n_pieces,
+                                         static_cast<const uint16_t*>(shard_flat), master, exp_avg, exp_avg_sq,
+                                         static_cast<hipStream_t>(stream)),
+                      "init-master kernel launch");
 }
 
 // ------------------------------------------------- (f4) offloaded Adam

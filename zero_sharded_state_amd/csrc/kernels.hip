@@ -918,6 +918,27 @@ __global__ __launch_bounds__(kBlock) void k_adam_inline(const AdamInline plan, f
     adam_piece<D, VEC>(b0 + begin, len, sub, threadIdx.x, w, m, v, g, s, scale, flag != 0, c);
 }
 
+// -------------------------------------------------- fp32 master partition
+// [codex] 6.1: the optimizer's fp32 partition is made from the rank's
+// 16-bit shard.  A span with `reserved` != 0 holds real positions (the
+// exact widening of the shard); other spans are padding (0).  Momentum and
+// variance start at 0 (each may be null: not written).  One-time set-up
+// work, so plain coalesced element accesses.
+template <int D>
+__global__ __launch_bounds__(kBlock) void k_init_master(const Span* __restrict__ spans,
+                                                        const uint16_t* __restrict__ shard, float* __restrict__ w,
+                                                        float* __restrict__ m, float* __restrict__ v) {
+    const uint32_t pidx = blockIdx.x / kAdamSub;
+    const int sub = static_cast<int>(blockIdx.x % kAdamSub);
+    const Span sp = spans[pidx];
+    for (int64_t i = int64_t(sub) * kBlock + threadIdx.x; i < sp.len; i += int64_t(kBlock) * kAdamSub) {
+        const int64_t e = sp.begin + i;
+        w[e] = sp.reserved != 0 ? widen<D>(shard[e]) : 0.0f;
+        if (m != nullptr) m[e] = 0.0f;
+        if (v != nullptr) v[e] = 0.0f;
+    }
+}
+
 inline dim3 grid_of(int64_t n) { return dim3(static_cast<uint32_t>(n)); }
 
 // Timing hook: when a host thread has set events, its next launch records
@@ -1108,6 +1129,15 @@ hipError_t launch_adam_inline(int32_t dtype, const AdamInline& plan, float* mast
         if (vec_ok) launch((k_adam_inline<kBF16, true>), g, b, stream, plan, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
         else launch((k_adam_inline<kBF16, false>), g, b, stream, plan, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_init_master(int32_t dtype, const Span* spans, int64_t n_spans, const uint16_t* shard,
+                              float* master, float* exp_avg, float* exp_avg_sq, hipStream_t stream) {
+    if (n_spans <= 0) return hipSuccess;
+    const dim3 g = grid_of(n_spans * kAdamSub), b(kBlock);
+    if (dtype == kFP16) launch(k_init_master<kFP16>, g, b, stream, spans, shard, master, exp_avg, exp_avg_sq);
+    else launch(k_init_master<kBF16>, g, b, stream, spans, shard, master, exp_avg, exp_avg_sq);
     return hipGetLastError();
 }
 

@@ -230,4 +230,9 @@ hipError_t launch_adam(int32_t dtype, const Span* spans, int64_t n_spans, float*
                        const float* scale, const int32_t* nonfinite, const AdamConsts& c,
                        bool vec_ok, hipStream_t stream);
 
+// master[e] = widen(shard[e]) over real spans (reserved != 0), 0 over the
+// others; exp_avg / exp_avg_sq (if not null) = 0 over every span.
+hipError_t launch_init_master(int32_t dtype, const Span* spans, int64_t n_spans, const uint16_t* shard,
+                              float* master, float* exp_avg, float* exp_avg_sq, hipStream_t stream);
+
 }  // namespace zs3

@@ -21,13 +21,15 @@ a few streams that fork from it and join back):
    persistent gradients take the all-reduce path either way.  With
    ``fuse_norm`` the reduce also writes the norm's partial sums of squares;
 4. the pre-step pass that puts every parameter back in partitioned form
-   ([codex] 6.3): the own range of each gathered parameter is copied into
-   the flat shard (it already holds those values, so the shard is
-   unchanged);
+   ([codex] 6.3): the gathered views are dropped.  The flat shard already
+   holds every parameter's own range, so no data moves (the partition copy
+   itself, ``repartition``, runs once at set-up);
 5. the global gradient norm and clip scale ([llmnex] pitfall 1), from
    grad_flat or, with ``fuse_norm``, from the reduce's partial sums;
 6. fused Adam + cast per sub-group, on the fp32 state in HBM or, with
-   ``offload``, in pinned host memory ([codex] 6.1, 6.3).
+   ``offload``, in pinned host memory ([codex] 6.1, 6.3).  Adam is the
+   only writer of the shard, so the shard is always the 16-bit rounding of
+   the fp32 master.
 
 No call synchronises; nothing is copied to the host.  All buffers are torch
 tensors owned by this object; all arithmetic runs in libzs3's kernels.
@@ -343,9 +345,13 @@ class ShardStep:
                                                   self.grad.data_ptr(), partials, handles[i % len(handles)]))
         self._join(main, aux)
 
-    def repartition(self, stream=None):
+    def repartition(self, stream=None, dst=None):
+        """The partition copy ([codex] 3.1): every full parameter's own range
+        into the flat shard (or into ``dst``, a buffer of the shard's size).
+        Set-up work: the step itself never copies parameters back."""
         n, ids, ptrs = self._p
-        self._ok(zs.lib().zs3_partition(self.h, self.rank, self.dcode, n, ids, ptrs, self.shard.data_ptr(),
+        out = self.shard if dst is None else dst
+        self._ok(zs.lib().zs3_partition(self.h, self.rank, self.dcode, n, ids, ptrs, out.data_ptr(),
                                         stream if stream is not None else self._stream()))
 
     def grad_norm(self, finalize: bool = True, stream=None):
@@ -395,8 +401,8 @@ class ShardStep:
             self.gather_pass(stream, gather_timer)
         mark("reduce_scatter")
         self.reduce_scatter(stream)
-        mark("partition")
-        self.repartition(stream)
+        # the pre-step pass ([codex] 6.3): the gathered views are dropped;
+        # the shard already is the partitioned form, so nothing moves
         mark("grad_norm")
         self.grad_norm(True, stream)
         mark("adam")
@@ -407,7 +413,9 @@ class ShardStep:
     def init_from_full(self):
         """Partition the gathered/persistent full parameters into the shard,
         fill every virtual rank's chunk of every wire buffer (what the
-        all-gather would deliver), and widen the shard into the fp32 master."""
+        all-gather would deliver), and build the fp32 optimizer partition
+        from the shard ([codex] 6.1: master = the shard widened, padding 0;
+        momentum and variance 0), all through the library's calls."""
         torch = self.torch
         tmp = torch.zeros_like(self.shard)
         n, ids, ptrs = self._p
@@ -419,11 +427,23 @@ class ShardStep:
             for bi, (bn, bids, _, _, _) in enumerate(self._g):
                 self._ok(lib.zs3_gather_coalesced(self.h, v, self.dcode, zs.ZS3_PACK, bn, bids, target.data_ptr(),
                                                   self.chunk_ptr(bi, v), None, None, None, s))
-        tdt = torch.float16 if self.dtype == "fp16" else torch.bfloat16
-        self.master.copy_(self.shard.view(tdt).to(torch.float32))
-        self.exp_avg.zero_()
-        self.exp_avg_sq.zero_()
         del tmp
+        if self.offload:
+            # built in HBM one sub-group at a time, then moved to the pinned host state
+            big = max((e - b for b, e in self.sub_groups), default=0)
+            w = torch.empty(max(1, big), dtype=torch.float32, device=self.device)
+            for b, e in self.sub_groups:
+                self._ok(lib.zs3_init_master(self.h, self.rank, self.dcode, b, e, self.shard.data_ptr(),
+                                             w.data_ptr() - 4 * b, None, None, s))
+                self.master[b:e].copy_(w[:e - b])
+            torch.cuda.current_stream().synchronize()
+            self.exp_avg.zero_()
+            self.exp_avg_sq.zero_()
+            return
+        for b, e in self.sub_groups:
+            self._ok(lib.zs3_init_master(self.h, self.rank, self.dcode, b, e, self.shard.data_ptr(),
+                                         self.master.data_ptr(), self.exp_avg.data_ptr(),
+                                         self.exp_avg_sq.data_ptr(), s))
 
     def fill_peer_norms(self):
         """Stand-in for the N-scalar all-reduce of the norm: after one partial
@@ -442,7 +462,6 @@ class ShardStep:
             "pack": 2 * 4 * part_real,          # two passes, read + write of the real own shard elements
             "unpack": 2 * 4 * F,                # two passes, read N pieces + write the full parameters
             "reduce_scatter": 2 * N * own + 2 * own,
-            "partition": 4 * own,
             "grad_norm": 0 if self.fuse_norm else 2 * own,    # fused: no second read of grad_flat
             "adam": 28 * own,
         }
@@ -455,14 +474,18 @@ class ShardStep:
 
     def budget_bytes(self) -> int:
         """The step's fixed algorithmic byte budget: forward and backward
-        gather (pack + unpack), the reduce-scatter, the re-partition, a norm
-        that reads the flat gradient once, and Adam -- the same work for every
-        variant of the step, so that effective bandwidth compares them at
-        equal work."""
+        gather (pack + unpack), the reduce-scatter, a norm that reads the
+        flat gradient once, and Adam -- the same work for every variant of
+        the step, so that effective bandwidth compares them at equal work."""
         N = self.N
         part_real = sum(p["own"][1] - p["own"][0] for p in self.params if not p["persistent"])
         own = self.own_real
-        return 2 * 4 * part_real + 2 * 4 * self.F + (2 * N + 2) * own + 4 * own + 2 * own + 28 * own
+        return 2 * 4 * part_real + 2 * 4 * self.F + (2 * N + 2) * own + 2 * own + 28 * own
+
+    def partition_bytes(self) -> int:
+        """The partition copy (set-up, not part of the step): read and write
+        every real own element once."""
+        return 4 * self.own_real
 
     def destroy(self):
         if self.h:
