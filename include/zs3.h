@@ -347,6 +347,22 @@ ZS3_API zs3_status zs3_grad_norm_partials(zs3_layout_t layout, int32_t rank, con
                                   double* sumsq, int32_t finalize, double max_norm, double loss_scale,
                                   double* norm_out, float* scale_out, int32_t* nonfinite, void* stream);
 
+/* For callers that cannot allocate device memory (work under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation as zs3_grad_norm_partials, with the same arguments and the
+ * same results bit for bit, that allocates nothing -- no hipMalloc, no
+ * hipFree, no layout table.  Its only scratch (the slot pass's per-workgroup
+ * sums, 16 KiB) is a static device array of the library: each GPU holds one
+ * copy until the process ends, found on the call's first use of that GPU.
+ * Every call on a GPU shares that copy, so calls that overlap on one GPU
+ * (on different streams, or from several host threads) race and may return
+ * wrong sums; serialise them.  Each call writes every scratch entry it
+ * reads, so nothing needs clearing between calls.  Limit: layouts with more
+ * than 1024 * 65536 norm slots (zs3_layout_norm_slots) get ZS3_EINVAL. */
+ZS3_API zs3_status zs3_grad_norm_partials_noalloc(zs3_layout_t layout, int32_t rank, const double* partials,
+                                          double* sumsq, int32_t finalize, double max_norm, double loss_scale,
+                                          double* norm_out, float* scale_out, int32_t* nonfinite, void* stream);
+
 /* ----------------------------------------- (5) fused Adam + 16-bit cast
  * [codex] 6.3: per sub-group, the rank's fp32 partition is stepped by the
  * real optimizer (it sees only this rank's shard) and the result is written

@@ -28,7 +28,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     syms = _declared_symbols()
-    assert len(syms) == 33
+    assert len(syms) == 34
     assert sorted(zs.EXPORTS) == syms
     for s in syms:
         assert hasattr(L, s), s
@@ -172,6 +172,9 @@ def test_call_validation_enqueues_nothing():
             (zs.ZS3_EINVAL, lambda: zs.zs3_grad_norm_partials(h, 0, base, base + 1 << 20, True, 0.0, 1.0,
                                                               base + 8192, base + 8200, base + 8204, stream=0)),
             (zs.ZS3_EALIAS, lambda: zs.zs3_grad_norm_partials(h, 0, base, base + 8, False, stream=0)),
+            (zs.ZS3_EINVAL, lambda: zs.zs3_grad_norm_partials_noalloc(h, 0, base + 4, base + 8192, False, stream=0)),
+            (zs.ZS3_EALIAS, lambda: zs.zs3_grad_norm_partials_noalloc(h, 0, base, base + 8, False, stream=0)),
+            (zs.ZS3_EINVAL, lambda: zs.zs3_grad_norm_partials_noalloc(h, 7, base, base + 8192, False, stream=0)),
             # the fp32 master partition
             (zs.ZS3_EINVAL, lambda: zs.zs3_init_master(h, 0, "bf16", 0, S + 1, base, base + (1 << 20), stream=0)),
             (zs.ZS3_EINVAL, lambda: zs.zs3_init_master(h, 0, "bf16", 5, 4, base, base + (1 << 20), stream=0)),
@@ -235,5 +238,23 @@ def test_norm_slots_cover_every_parameter(name):
         n_slots, n_part = zs.zs3_layout_norm_slots(h)
         assert n_part == _slot_count([p.partition_size for p in ol.params if not p.persistent])
         assert n_slots == n_part + _slot_count([p.partition_size for p in ol.params if p.persistent])
+    finally:
+        zs.zs3_layout_destroy(h)
+
+
+def test_noalloc_norm_rejects_layouts_past_its_scratch():
+    """The allocation-free norm's limit is checked before any device work: a
+    layout whose slot array is larger than 1024 * 65536 slots is refused
+    with a message (the layout itself is host-only, never allocated)."""
+    h = zs.zs3_layout_create(1, 0, [0], [1 << 37])
+    try:
+        n_slots, _ = zs.zs3_layout_norm_slots(h)
+        assert n_slots > 1024 * 65536
+        base = 1 << 40     # fake, never dereferenced
+        with pytest.raises(zs.Zs3Error) as e:
+            zs.zs3_grad_norm_partials_noalloc(h, 0, base, base + 8 * n_slots + 4096, True, 1.0, 1.0,
+                                              base + 8 * n_slots + 8192, base + 8 * n_slots + 8200,
+                                              base + 8 * n_slots + 8204, stream=0)
+        assert e.value.status == zs.ZS3_EINVAL and "at most" in e.value.message
     finally:
         zs.zs3_layout_destroy(h)

@@ -47,6 +47,7 @@ EXPORTS = (
     "zs3_layout_param", "zs3_layout_own_range", "zs3_plan_buckets", "zs3_sub_groups",
     "zs3_bucket_sizes", "zs3_partition", "zs3_gather_coalesced", "zs3_reduce_scatter_local",
     "zs3_layout_norm_slots", "zs3_reduce_scatter_coalesced", "zs3_grad_norm", "zs3_grad_norm_partials",
+    "zs3_grad_norm_partials_noalloc",
     "zs3_adam_step", "zs3_adam_step_offload", "zs3_init_master", "zs3_coord_create", "zs3_coord_destroy",
     "zs3_coord_fetch", "zs3_coord_release",
     "zs3_coord_release_all", "zs3_coord_reset_step", "zs3_coord_info", "zs3_coord_param_status",
@@ -113,6 +114,8 @@ _SIGNATURES = {
                                               _c_p, ctypes.POINTER(_c_p), _c_p, _c_p, _c_p]),
     "zs3_grad_norm_partials": (_c_i32, [_c_p, _c_i32, _c_p, _c_p, _c_i32, ctypes.c_double, ctypes.c_double,
                                         _c_p, _c_p, _c_p, _c_p]),
+    "zs3_grad_norm_partials_noalloc": (_c_i32, [_c_p, _c_i32, _c_p, _c_p, _c_i32, ctypes.c_double, ctypes.c_double,
+                                                _c_p, _c_p, _c_p, _c_p]),
     "zs3_grad_norm": (_c_i32, [_c_p, _c_i32, _c_i32, _c_p, _c_p, _c_i32, ctypes.c_double,
                                ctypes.c_double, _c_p, _c_p, _c_p, _c_p]),
     "zs3_adam_step": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
@@ -345,6 +348,14 @@ def zs3_grad_norm_partials(layout: int, rank: int, partials, sumsq, finalize: bo
     _check(lib().zs3_grad_norm_partials(layout, rank, _ptr(partials), _ptr(sumsq), int(bool(finalize)),
                                         float(max_norm), float(loss_scale), _ptr(norm_out), _ptr(scale_out),
                                         _ptr(nonfinite), _stream(stream)))
+
+
+def zs3_grad_norm_partials_noalloc(layout: int, rank: int, partials, sumsq, finalize: bool, max_norm: float = 1.0,
+                                   loss_scale: float = 1.0, norm_out=None, scale_out=None, nonfinite=None,
+                                   stream=None) -> None:
+    _check(lib().zs3_grad_norm_partials_noalloc(layout, rank, _ptr(partials), _ptr(sumsq), int(bool(finalize)),
+                                                float(max_norm), float(loss_scale), _ptr(norm_out), _ptr(scale_out),
+                                                _ptr(nonfinite), _stream(stream)))
 
 
 def zs3_adam_step(layout: int, rank: int, dtype, begin: int, end: int, master, exp_avg, exp_avg_sq, grad_flat,

@@ -1121,9 +1121,14 @@ zs3_status zs3_layout_norm_slots(zs3_layout_t L, int64_t* n_slots, int64_t* n_pa
     return ok();
 }
 
-zs3_status zs3_grad_norm_partials(zs3_layout_t L, int32_t rank, const double* partials, double* sumsq,
-                                  int32_t finalize, double max_norm, double loss_scale, double* norm_out,
-                                  float* scale_out, int32_t* nonfinite, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Arguments of the two slot-norm entry points.
+zs3_status check_norm_partials(const zs3_layout* L, int32_t rank, const double* partials, const double* sumsq,
+                               int32_t finalize, double max_norm, double loss_scale, const double* norm_out,
+                               const float* scale_out, const int32_t* nonfinite) {
     zs3_status s = check_layout_rank(L, rank);
     if (s != ZS3_OK) return s;
     if (partials == nullptr || !aligned(partials, 8)) return fail(ZS3_EINVAL, "partials is NULL or not 8-byte aligned");
@@ -1136,13 +1141,29 @@ zs3_status zs3_grad_norm_partials(zs3_layout_t L, int32_t rank, const double* pa
         if (!(max_norm > 0.0) || !(loss_scale > 0.0)) return fail(ZS3_EINVAL, "max_norm and loss_scale must be > 0");
     }
     if (overlap(sumsq, 8 * (L->world + 1), partials, 8 * L->n_slots)) return fail(ZS3_EALIAS, "sumsq overlaps partials");
+    return ZS3_OK;
+}
+
+// The allocation-free slot norm sums at most this many slots per call
+// (its scratch holds kNormSlotBlocks workgroup sums; beyond this bound each
+// workgroup would walk more than 65536 slots).
+constexpr int64_t kNoAllocMaxSlots = kNormSlotBlocks * 65536;
+
+}  // namespace
+
+extern "C" {
+
+zs3_status zs3_grad_norm_partials(zs3_layout_t L, int32_t rank, const double* partials, double* sumsq,
+                                  int32_t finalize, double max_norm, double loss_scale, double* norm_out,
+                                  float* scale_out, int32_t* nonfinite, void* stream) {
+    zs3_status s = check_norm_partials(L, rank, partials, sumsq, finalize, max_norm, loss_scale, norm_out, scale_out,
+                                       nonfinite);
+    if (s != ZS3_OK) return s;
     Key key{{kOpNormSlots, device_id(), reinterpret_cast<int64_t>(stream)}};     // scratch per stream, as above
     Plan* plan = find_plan(L, key);
     if (plan == nullptr) {
         Plan np;
-        // about 1024 slots per workgroup, at most 1024 workgroups
-        np.n_blocks = std::max<int64_t>(1, std::min<int64_t>(1024, (L->n_slots + 1023) / 1024));
-        np.n_pieces = (L->n_slots + np.n_blocks - 1) / np.n_blocks;    // slots per workgroup
+        norm_slot_split(L->n_slots, &np.n_blocks, &np.n_pieces);    // n_pieces: slots per workgroup
         std::vector<size_t> offs;
         s = upload(&np, {}, 2 * static_cast<size_t>(np.n_blocks) * sizeof(double), &offs);
         if (s != ZS3_OK) return s;
@@ -1152,6 +1173,21 @@ zs3_status zs3_grad_norm_partials(zs3_layout_t L, int32_t rank, const double* pa
                                              plan->at<double>(plan->off_scratch), sumsq, rank, L->world, finalize,
                                              max_norm, loss_scale, norm_out, scale_out, nonfinite,
                                              static_cast<hipStream_t>(stream)),
+                      "grad-norm kernel launch");
+}
+
+zs3_status zs3_grad_norm_partials_noalloc(zs3_layout_t L, int32_t rank, const double* partials, double* sumsq,
+                                          int32_t finalize, double max_norm, double loss_scale, double* norm_out,
+                                          float* scale_out, int32_t* nonfinite, void* stream) {
+    zs3_status s = check_norm_partials(L, rank, partials, sumsq, finalize, max_norm, loss_scale, norm_out, scale_out,
+                                       nonfinite);
+    if (s != ZS3_OK) return s;
+    if (L->n_slots > kNoAllocMaxSlots)
+        return fail(ZS3_EINVAL, "layout has %lld norm slots; the allocation-free norm sums at most %lld",
+                    (long long)L->n_slots, (long long)kNoAllocMaxSlots);
+    return hip_status(launch_norm_from_slots_static(partials, L->n_slots, L->n_part_slots, sumsq, rank, L->world,
+                                                    finalize, max_norm, loss_scale, norm_out, scale_out, nonfinite,
+                                                    static_cast<hipStream_t>(stream)),
                       "grad-norm kernel launch");
 }
 

@@ -19,7 +19,17 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "zs3_internal.hpp"
+
+// Scratch of the allocation-free norm entry point: the slot pass's two
+// sums (partitioned, persistent) per workgroup, at most kNormSlotBlocks
+// workgroups: 16 KiB.  Every GPU the library runs on holds its own copy
+// until the process ends; every call on that GPU shares it.  In host code
+// this name is only a stand-in for the symbol: kernels get the per-device
+// address that hipGetSymbolAddress returns (static_norm_scratch below).
+static __device__ __align__(256) double scratch[2 * zs3::kNormSlotBlocks];
 
 namespace zs3 {
 namespace {
@@ -1082,6 +1092,45 @@ hipError_t launch_norm_from_slots(const double* partials, int64_t n_slots, int64
     launch(k_norm_finalize, dim3(1), dim3(kBlock), stream, static_cast<const double*>(block_sums), n_blocks, sumsq,
            rank, world, finalize, max_norm, loss_scale, norm_out, scale_out, nonfinite);
     return hipGetLastError();
+}
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current (each GPU's copy has its own address).
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+double* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static hipError_t static_norm_scratch(double** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<double*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_norm_from_slots_static(const double* partials, int64_t n_slots, int64_t n_part, double* sumsq,
+                                         int32_t rank, int32_t world, int32_t finalize, double max_norm,
+                                         double loss_scale, double* norm_out, float* scale_out, int32_t* nonfinite,
+                                         hipStream_t stream) {
+    double* block_sums = nullptr;
+    const hipError_t e = static_norm_scratch(&block_sums);
+    if (e != hipSuccess) return e;
+    int64_t n_blocks, per_block;
+    norm_slot_split(n_slots, &n_blocks, &per_block);
+    // every block sum the finalize pass reads is written by this call's slot
+    // pass, so nothing left in the scratch by an earlier call is ever read
+    return launch_norm_from_slots(partials, n_slots, n_part, n_blocks, per_block, block_sums, sumsq, rank, world,
+                                  finalize, max_norm, loss_scale, norm_out, scale_out, nonfinite, stream);
 }
 
 hipError_t launch_grad_norm(int32_t dtype, const uint16_t* grad, const Span* spans, int64_t n_spans,

@@ -212,6 +212,27 @@ hipError_t launch_norm_from_slots(const double* partials, int64_t n_slots, int64
                                   int32_t world, int32_t finalize, double max_norm, double loss_scale,
                                   double* norm_out, float* scale_out, int32_t* nonfinite, hipStream_t stream);
 
+// How the slot pass splits a slot array: about 1024 slots per workgroup, at
+// most kNormSlotBlocks workgroups (the same split for every caller, so the
+// allocation-free entry point sums in the same order as the cached one).
+constexpr int64_t kNormSlotBlocks = 1024;
+inline void norm_slot_split(int64_t n_slots, int64_t* n_blocks, int64_t* per_block) {
+    int64_t b = (n_slots + 1023) / 1024;
+    if (b > kNormSlotBlocks) b = kNormSlotBlocks;
+    if (b < 1) b = 1;
+    *n_blocks = b;
+    *per_block = (n_slots + b - 1) / b;
+}
+
+// The allocation-free form of launch_norm_from_slots: the per-workgroup sums
+// live in the library's static device array (2 * kNormSlotBlocks doubles per
+// device) instead of caller- or layout-owned scratch.  Its address is looked
+// up once per device (the first call with that device current).
+hipError_t launch_norm_from_slots_static(const double* partials, int64_t n_slots, int64_t n_part, double* sumsq,
+                                         int32_t rank, int32_t world, int32_t finalize, double max_norm,
+                                         double loss_scale, double* norm_out, float* scale_out, int32_t* nonfinite,
+                                         hipStream_t stream);
+
 // Sums of squares of grad over the spans ([0, n_part) partitioned, the rest
 // persistent) by n_blocks workgroups into partials[2*n_blocks], then one
 // workgroup combines them into sumsq[rank], sumsq[world] and, if finalize,
