@@ -13,8 +13,10 @@ data-parallel ranks are N virtual ranks in this GPU's HBM; inputs are
 synthetic (seeded N(0, 0.02) weights, N(0, 1e-3) gradients with 1% x100
 outliers) and resident in HBM before timing starts.
 
-Default launch configuration: gather buckets back to back on one stream,
-gradient buckets over three streams, the norm fused into the reduce.
+Default launch configuration: gather buckets dealt over two streams,
+gradient buckets over three streams, the slices each rank receives placed
+per gradient bucket, the norm fused into the reduce.  --single-launch
+gather|reduce|both makes a phase one launch over every bucket.
 Variants: --reduce-path coalesced (the non-contiguous gradient path),
 --schedule trace (gathers driven by the fetch/release coordinator over the
 forward+backward module order), --offload 1 (the fp32 optimizer state in
@@ -62,8 +64,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=12, help="decoder layers in the oracle's sample")
     ap.add_argument("--rs-streams", type=int, default=3, help="streams the gradient buckets are spread over")
-    ap.add_argument("--gather-streams", type=int, default=1, help="streams the gather buckets are spread over")
-    ap.add_argument("--no-kernel-timer", action="store_true", help="do not time the gather launches")
+    ap.add_argument("--gather-streams", type=int, default=2, help="streams the gather buckets are spread over")
+    ap.add_argument("--kernel-timer", action="store_true",
+                    help="with several gather streams, also time every gather launch of the timed steps")
     ap.add_argument("--fuse-norm", type=int, default=1, choices=(0, 1),
                     help="1: the reduce-scatter also writes the norm's partial sums (no second read of grad_flat)")
     ap.add_argument("--reduce-path", default="contiguous", choices=("contiguous", "coalesced"),
@@ -81,6 +84,12 @@ def parse():
     ap.add_argument("--reduce-bucket-size", type=float, default=None,
                     help="gradient bucket limit in full elements (default: the workload's); larger than the "
                          "model makes the gradient phase one launch")
+    ap.add_argument("--recv-layout", default="bucket", choices=("rank", "bucket"),
+                    help="where the slices the N ranks send this rank live: one shard-shaped copy per rank, or "
+                         "per gradient bucket with its N slices next to each other")
+    ap.add_argument("--single-launch", default="none", choices=("none", "gather", "reduce", "both"),
+                    help="gather: each gather pass one launch over every bucket (each bucket keeps its own wire and "
+                         "gathered buffer); reduce: the gradient phase one launch over every bucket; both")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -164,7 +173,7 @@ def with_bucket_sizes(cfg, prefetch=None, reduce=None):
 
 
 def make_step(cfg, rank, rs_streams=1, gather_streams=1, fuse_norm=False, reduce_path="contiguous", offload=False,
-              offload_chunk=0):
+              offload_chunk=0, recv_layout="rank", single_launch="none"):
     from zero_sharded_state_amd.shard_step import AdamConfig, ShardStep
 
     return ShardStep(world_size=cfg.world_size, rank=rank, threshold=cfg.threshold, ds_ids=cfg.ds_ids,
@@ -172,7 +181,8 @@ def make_step(cfg, rank, rs_streams=1, gather_streams=1, fuse_norm=False, reduce
                      reduce_bucket_size=cfg.reduce_bucket_size, sub_group_size=cfg.sub_group_size,
                      adam=AdamConfig(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay),
                      max_norm=cfg.max_norm, rs_streams=rs_streams, gather_streams=gather_streams,
-                     fuse_norm=fuse_norm, reduce_path=reduce_path, offload=offload, offload_chunk=offload_chunk)
+                     fuse_norm=fuse_norm, reduce_path=reduce_path, offload=offload, offload_chunk=offload_chunk,
+                     recv_layout=recv_layout, single_launch=single_launch)
 
 
 def fill_inputs(step, cfg):
@@ -250,7 +260,7 @@ def cpu_baseline(step, cfg, layers: int):
             p = step.by_id[d]
             lo, hi = p["own"]
             a = np.zeros(p["numel"], np.uint16)
-            o = v * step.recv_stride + p["shard_offset"]
+            o = step.recv_index(v, d)
             a[lo:hi] = h16(step.recv[o:o + (hi - lo)])
             g[d] = a
         grads.append(g)
@@ -368,7 +378,7 @@ def main():
     rank = cfg.bench_rank if args.rank is None else args.rank
     log(f"config {cfg.name}: {cfg.title}, rank {rank}")
     step = make_step(cfg, rank, args.rs_streams, args.gather_streams, bool(args.fuse_norm), args.reduce_path,
-                     bool(args.offload), args.offload_chunk)
+                     bool(args.offload), args.offload_chunk, args.recv_layout, args.single_launch)
     log(f"layout: S+P={step.S:,} own real={step.own_real:,} F={step.F:,} gather buckets={len(step.gather_buckets)} "
         f"reduce buckets={len(step.reduce_buckets)} sub-groups={len(step.sub_groups)}")
     t0 = time.time()
@@ -405,12 +415,12 @@ def main():
         e.record(stream)
         phase_events[-1].append((name, e))
 
-    # One gather stream: launches run back to back, so the gather phases'
-    # event time over the launch count is the average kernel duration (it
-    # matches rocprofv3's).  Several streams overlap launches: then every
-    # launch records its own start/end (this costs a few us per launch).
-    per_launch = step.gather_streams > 1 and not args.no_kernel_timer
-    timer = KernelTimer(2 * len(step.gather_buckets) * args.steps if per_launch else 0)
+    # With --kernel-timer and several gather streams every gather launch of
+    # the timed steps records its own start/end (a few us per launch).
+    per_pass = 1 if step.single_gather else len(step.gather_buckets)
+    overlapped = step.gather_streams > 1 and not step.single_gather and trace is None
+    per_launch = overlapped and args.kernel_timer
+    timer = KernelTimer(2 * per_pass * args.steps if per_launch else 0)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(args.steps):
@@ -452,24 +462,51 @@ def main():
                                       if phase_bytes[name] else None)}
 
     # Roofline entry of the dominant kernel: the fused gather (pack + unpack
-    # of one bucket, k_copy<4>), average duration over the timed launches.
-    launches = (len(trace.ops) if trace is not None else 2 * len(step.gather_buckets)) * args.steps
-    if per_launch:
-        durs = timer.durations_ms()
-        avg_ms = sum(durs) / len(durs)
-    else:
-        avg_ms = sum(phases.get(k, 0.0) for k in ("gather_fwd", "gather_bwd", "gather_trace")) / launches
-    timer.close()
+    # of one bucket, k_copy<4>), bytes per launch over the average launch
+    # duration.  When the step runs its gather launches back to back on one
+    # stream, that is the gather phases' event time on the launch stream over
+    # the launch count (it matches rocprofv3's average).  When the step deals
+    # them over several streams, launches overlap in pairs and each lasts
+    # about twice as long while sharing the chip, so the kernel's own
+    # duration is taken from gather passes run on the launch stream alone
+    # right after the timed steps (the same launches on the same buffers).
     gather_bytes = nbytes["gather_trace"] if trace is not None else nbytes["pack"] + nbytes["unpack"]
-    per_launch_bytes = gather_bytes * args.steps / launches
+    gather_phase_ms = sum(phases.get(k, 0.0) for k in ("gather_fwd", "gather_bwd", "gather_trace"))
+    if overlapped:
+        cal_passes = 2 * min(args.steps, 5)
+        step.gather_pass(streams=1)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(cal_passes):
+            step.gather_pass(streams=1)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        launches = cal_passes * per_pass
+        avg_ms = e0.elapsed_time(e1) / launches
+        per_launch_bytes = gather_bytes / 2 / per_pass
+        measured = (f"{cal_passes} gather passes on the launch stream alone, right after the timed steps "
+                    f"(the step deals its buckets over {step.gather_streams} streams)")
+    else:
+        launches = (len(trace.ops) if trace is not None else 2 * per_pass) * args.steps
+        avg_ms = gather_phase_ms / launches
+        per_launch_bytes = gather_bytes * args.steps / launches
+        measured = "the timed steps' gather phases on the launch stream"
     achieved = per_launch_bytes / (avg_ms * 1e-3) / 1e9
-    roofline = {"kernel": "gather: pack + unpack of one bucket (k_copy_inline<4>)", "bound": "hbm",
+    unit = "every bucket of a pass" if step.single_gather else "one bucket"
+    roofline = {"kernel": f"gather: pack + unpack of {unit} (k_copy_inline<4>, or k_copy<4> for > 40 segments)",
+                "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_entry(cfg.name) if trace is None else None,
                 "launches": launches, "avg_launch_ms": round(avg_ms, 5),
                 "algorithmic_bytes_per_launch": int(per_launch_bytes),
-                "streams": step.gather_streams}
+                "measured_on": measured,
+                "step_gather": {"streams": step.gather_streams,
+                                "GBps": round(gather_bytes * args.steps / (gather_phase_ms * 1e-3) / 1e9, 1)}}
+    if per_launch:
+        durs = timer.durations_ms()
+        roofline["step_gather"]["avg_launch_ms_overlapped"] = round(sum(durs) / len(durs), 5)
+    timer.close()
 
     # The partition copy (construction-time, not part of the step): every
     # full parameter's own range into a scratch shard, timed on its own.
@@ -554,7 +591,8 @@ def main():
             "reduce_bucket_size": cfg.reduce_bucket_size, "sub_group_size": cfg.sub_group_size,
             "reduce_path": step.reduce_path, "fused_norm": step.fuse_norm, "rs_streams": step.rs_streams,
             "schedule": args.schedule, "offload": step.offload,
-            "gather_streams": step.gather_streams,
+            "gather_streams": step.gather_streams, "recv_layout": step.recv_layout,
+            "single_launch": step.single_launch,
         },
         "kernels": kernels,
         "roofline": roofline,

@@ -234,6 +234,27 @@ ZS3_API zs3_status zs3_gather_coalesced(zs3_layout_t layout, int32_t rank, int32
                                 void* own_chunk, const void* const* rank_chunks, void* full_flat,
                                 int64_t* full_offsets, void* stream);
 
+/* Several gather buckets in one launch.  [codex] 5.2: each prefetch fills one
+ * bucket and gathers it with one coalesced collective; [llmnex] section 4
+ * (pitfalls): buckets that are too small make the step latency-bound.  This
+ * call does exactly what n_buckets calls of zs3_gather_coalesced with
+ * mode = ZS3_PACK | ZS3_UNPACK (the wire's own slot being the pack's
+ * output) would do, bucket by bucket, with the same results bit for bit,
+ * but as one kernel launch.
+ * Bucket b is ds_ids[bucket_start[b] .. bucket_start[b+1]) (host; any order
+ * inside a bucket, none persistent, no ds_id in two buckets; bucket_start
+ * has n_buckets+1 increasing entries from 0).  own_chunks[b] and
+ * full_flats[b] (host arrays of n_buckets dev pointers) are bucket b's
+ * own_chunk and full_flat; rank_chunks (host, n_buckets*N dev pointers)
+ * holds bucket b's N chunk pointers at [b*N .. b*N+N), with
+ * rank_chunks[b*N + rank] == own_chunks[b].  shard_flat: dev, the rank's
+ * flat shard.  No written buffer may overlap any other buffer of the call.
+ */
+ZS3_API zs3_status zs3_gather_coalesced_buckets(zs3_layout_t layout, int32_t rank, int32_t dtype, int32_t n_buckets,
+                                        const int32_t* bucket_start, const int64_t* ds_ids, const void* shard_flat,
+                                        void* const* own_chunks, const void* const* rank_chunks,
+                                        void* const* full_flats, void* stream);
+
 /* ------------------------------------------ (3) local reduce-scatter
  * [codex] 6.2: the contiguous-gradient path all-reduces the bucket and each
  * rank keeps only its own interval, written into the one contiguous flat

@@ -28,7 +28,7 @@ def L():
 
 def test_library_exports_every_declared_symbol(L):
     syms = _declared_symbols()
-    assert len(syms) == 34
+    assert len(syms) == 35
     assert sorted(zs.EXPORTS) == syms
     for s in syms:
         assert hasattr(L, s), s
@@ -175,6 +175,33 @@ def test_call_validation_enqueues_nothing():
             (zs.ZS3_EINVAL, lambda: zs.zs3_grad_norm_partials_noalloc(h, 0, base + 4, base + 8192, False, stream=0)),
             (zs.ZS3_EALIAS, lambda: zs.zs3_grad_norm_partials_noalloc(h, 0, base, base + 8, False, stream=0)),
             (zs.ZS3_EINVAL, lambda: zs.zs3_grad_norm_partials_noalloc(h, 7, base, base + 8192, False, stream=0)),
+            # several gather buckets in one launch
+            (zs.ZS3_EINVAL, lambda: zs.zs3_gather_coalesced_buckets(h, 0, "bf16", [[0], []], base,
+                                                                    [base + 4096, base + 8192],
+                                                                    [[base + 4096] * 4, [base + 8192] * 4],
+                                                                    [base + 65536, base + 131072], stream=0)),
+            (zs.ZS3_EDUPID, lambda: zs.zs3_gather_coalesced_buckets(h, 0, "bf16", [[0], [2, 0]], base,
+                                                                    [base + 4096, base + 8192],
+                                                                    [[base + 4096] + [base + 16384] * 3,
+                                                                     [base + 8192] + [base + 24576] * 3],
+                                                                    [base + 65536, base + 131072], stream=0)),
+            (zs.ZS3_EPERSIST, lambda: zs.zs3_gather_coalesced_buckets(h, 0, "bf16", [[1]], base, [base + 4096],
+                                                                      [[base + 4096] * 4], [base + 65536],
+                                                                      stream=0)),
+            (zs.ZS3_EINVAL, lambda: zs.zs3_gather_coalesced_buckets(h, 0, "bf16", [[0]], base, [base + 4096],
+                                                                    [[base + 8192] * 4], [base + 65536], stream=0)),
+            # bucket 1's gathered buffer overlaps bucket 0's own chunk
+            (zs.ZS3_EALIAS, lambda: zs.zs3_gather_coalesced_buckets(h, 0, "bf16", [[0], [2]], base,
+                                                                    [base + 4096, base + 8192],
+                                                                    [[base + 4096] + [base + 16384] * 3,
+                                                                     [base + 8192] + [base + 24576] * 3],
+                                                                    [base + 65536, base + 4100], stream=0)),
+            # a peer's chunk of bucket 1 overlaps bucket 0's gathered buffer
+            (zs.ZS3_EALIAS, lambda: zs.zs3_gather_coalesced_buckets(h, 0, "bf16", [[0], [2]], base,
+                                                                    [base + 4096, base + 8192],
+                                                                    [[base + 4096] + [base + 16384] * 3,
+                                                                     [base + 8192] + [base + 65600] * 3],
+                                                                    [base + 65536, base + 131072], stream=0)),
             # the fp32 master partition
             (zs.ZS3_EINVAL, lambda: zs.zs3_init_master(h, 0, "bf16", 0, S + 1, base, base + (1 << 20), stream=0)),
             (zs.ZS3_EINVAL, lambda: zs.zs3_init_master(h, 0, "bf16", 5, 4, base, base + (1 << 20), stream=0)),
@@ -219,6 +246,7 @@ def test_call_validation_enqueues_nothing():
         zs.zs3_reduce_scatter_coalesced(h, 0, "fp16", zs.ZS3_PACK | zs.ZS3_REDUCE, [], grads=[], send=base,
                                         recv_chunks=[base] * 4, grad_flat=base + 65536, stream=0)
         zs.zs3_init_master(h, 0, "fp16", 3, 3, base, base + (1 << 20), stream=0)
+        zs.zs3_gather_coalesced_buckets(h, 0, "fp16", [], base, [], [], [], stream=0)
     finally:
         zs.zs3_layout_destroy(h)
 

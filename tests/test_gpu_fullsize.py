@@ -61,14 +61,14 @@ def _recv_grads(step, L, host_recv):
     """Oracle-side gradients: virtual rank v's full gradient of every
     parameter, zero except the slice this rank receives (the oracle reads
     only that slice)."""
-    N, S = step.N, step.recv_stride
+    N = step.N
     grads = []
     for v in range(N):
         g = {}
         for p in L.params:
             lo, hi = L.own_range(p, step.rank)
             a = np.zeros(p.numel, np.uint16)
-            o = v * S + p.shard_offset
+            o = step.recv_index(v, p.ds_id)
             a[lo:hi] = host_recv[o:o + (hi - lo)]
             g[p.ds_id] = a
         grads.append(g)
@@ -275,7 +275,7 @@ def test_fullsize_calls_on_sampled_parameters(name, rank):
             grads = []
             for v in range(N):
                 a = np.zeros(p.numel, np.uint16)
-                o = v * step.recv_stride + p.shard_offset
+                o = step.recv_index(v, p.ds_id)
                 a[lo:hi] = h16(step.recv[o:o + (hi - lo)])
                 grads.append({d: a})
             sub = oracle.make_layout(N, cfg.threshold, [d], [p.numel])

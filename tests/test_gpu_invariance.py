@@ -148,3 +148,102 @@ def test_adam_does_not_depend_on_sub_groups(case):
             assert np.array_equal(a, b), name
     finally:
         zs.zs3_layout_destroy(h)
+
+
+# ------------------------------------------------------- one launch per phase
+
+@pytest.mark.parametrize("seed", range(30))
+def test_gather_buckets_in_one_launch(seed):
+    """zs3_gather_coalesced_buckets: random layouts split into random
+    buckets (shuffled inside), each bucket's wire and gathered buffer at its
+    own misaligned place: every packed chunk and gathered buffer equals the
+    per-bucket calls' and the oracle's pack + unpack, bit for bit; canaries
+    intact."""
+    rng = np.random.default_rng(700 + seed)
+    N = int(rng.choice([1, 2, 3, 5, 8, 16, 64]))
+    T = int(rng.choice([0, 50, 500]))
+    n = int(rng.integers(1, 40))
+    numels = [int(rng.integers(1, 300)) if k < 0.5 else int(rng.integers(300, 60_000)) for k in rng.random(n)]
+    ids = [int(x) for x in rng.choice(8 * n + 3, n, replace=False)]
+    dtype = "bf16" if rng.random() < 0.5 else "fp16"
+    r = int(rng.integers(0, N))
+    h = zs.zs3_layout_create(N, T, ids, numels)
+    L = oracle.make_layout(N, T, ids, numels)
+    try:
+        full = {d: random_bits16(seed, nm, dtype, 0.02, 3, d) for d, nm in zip(ids, numels)}
+        shards = [oracle.partition(L, v, full) for v in range(N)]
+        part = [int(x) for x in rng.permutation([p.ds_id for p in L.params if not p.persistent])]
+        if not part:
+            return
+        cuts = sorted(set(int(x) for x in rng.integers(1, len(part) + 1, int(rng.integers(0, 6)))) | {len(part)})
+        buckets, a = [], 0
+        for c in cuts:
+            buckets.append(part[a:c])
+            a = c
+        sh = Buf16(L.shard_numel, shift=int(rng.integers(0, 8)), fill=shards[r])
+        tag = f"gather buckets seed={seed} N={N} {dtype} rank={r} buckets={[len(b) for b in buckets]}"
+        res = {}
+        for label in ("per bucket", "one launch"):
+            owns, fulls, chunks, keep = [], [], [], []
+            for b in buckets:
+                chunk_n, full_n = oracle.bucket_sizes(L, b)
+                ref_chunks = [oracle.pack(L, v, b, shards[v]) for v in range(N)]
+                cb = [Buf16(chunk_n, shift=int(rng.integers(0, 8)), fill=ref_chunks[v]) for v in range(N)]
+                own = Buf16(chunk_n, shift=int(rng.integers(0, 8)))
+                fl = Buf16(full_n, shift=int(rng.integers(0, 8)))
+                ptrs = [c.ptr() for c in cb]
+                ptrs[r] = own.ptr()
+                owns.append(own)
+                fulls.append(fl)
+                chunks.append(ptrs)
+                keep.append(cb)
+            note(f"{tag}: {label}")
+            if label == "per bucket":
+                for b, own, ptrs, fl in zip(buckets, owns, chunks, fulls):
+                    zs.zs3_gather_coalesced(h, r, dtype, zs.ZS3_PACK | zs.ZS3_UNPACK, b, sh.ptr(), own.ptr(), ptrs,
+                                            fl.ptr())
+            else:
+                zs.zs3_gather_coalesced_buckets(h, r, dtype, buckets, sh.ptr(), [o.ptr() for o in owns], chunks,
+                                                [f.ptr() for f in fulls])
+            sync()
+            res[label] = [(o.host(), f.host()) for o, f in zip(owns, fulls)]
+            for buf in owns + fulls:
+                buf.check_guards()
+        for bi, b in enumerate(buckets):
+            ref_chunks = [oracle.pack(L, v, b, shards[v]) for v in range(N)]
+            ref_full, _ = oracle.unpack(L, b, ref_chunks)
+            for label in res:
+                own, fl = res[label][bi]
+                assert np.array_equal(own, ref_chunks[r]), f"{label}: packed chunk of bucket {bi}"
+                assert np.array_equal(fl, ref_full), f"{label}: gathered bucket {bi}"
+    finally:
+        zs.zs3_layout_destroy(h)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,rank", [("c2", 0), ("c3", 7), ("c1", 2)])
+def test_single_launch_step_equals_per_bucket_step(name, rank):
+    """A whole step with one gather launch per pass and one reduce-scatter
+    launch for every gradient bucket gives the bits of the per-bucket step:
+    every gathered buffer, the flat gradient, the fused norm's partial sums,
+    the norm and the fp32 state and 16-bit shard after two steps."""
+    import bench
+    from synth import get_config
+
+    cfg = get_config(name)
+    out = {}
+    for single in (False, True):
+        note(f"single-launch step {name} rank={rank} single={single}")
+        step = bench.make_step(cfg, rank, rs_streams=3, fuse_norm=True, single_launch=single)
+        try:
+            bench.fill_inputs(step, cfg)
+            for _ in range(2):
+                step.step()
+            sync()
+            out[single] = {k: getattr(step, k).cpu().numpy().view(np.uint8).copy()
+                           for k in ("full", "wire", "grad", "partials", "sumsq", "outs", "master", "exp_avg",
+                                     "exp_avg_sq", "shard")}
+        finally:
+            step.destroy()
+    for k in out[False]:
+        assert np.array_equal(out[False][k], out[True][k]), f"{k} differs between the two launch modes"

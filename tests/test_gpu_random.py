@@ -353,3 +353,120 @@ def test_random_layout_init_master(seed):
         assert np.all(M2.host() == 7.0)
     finally:
         zs.zs3_layout_destroy(h)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_layout_wide_reduce_scatter(seed):
+    """Many ranks (16 to 100) with every source co-aligned with its
+    destination modulo 16 bytes (the layout the wide reduce-scatter kernel
+    takes): random ragged layouts and buckets, both gradient paths, the
+    fused norm's slots pre-filled with NaN.  The flat gradient equals the
+    oracle's reduce-scatter bit for bit and the partial sums of squares its
+    shard-aware partials within 1e-12."""
+    import torch
+    rng = np.random.default_rng(30_000 + seed)
+    N = int(rng.choice([16, 17, 31, 64, 64, 100]))
+    T = int(rng.choice([0, 100, 5000]))
+    n = int(rng.integers(1, 12))
+    numels = [int(rng.integers(1, 3000)) if k < 0.4 else int(rng.integers(3000, 400_000)) if k < 0.9
+              else int(rng.integers(400_000, 4_000_000)) for k in rng.random(n)]
+    ids = [int(x) for x in rng.choice(6 * n + 5, n, replace=False)]
+    dtype = "bf16" if rng.random() < 0.5 else "fp16"
+    r = int(rng.choice([0, N - 1, int(rng.integers(0, N))]))
+    path = "coalesced" if rng.random() < 0.35 else "contiguous"
+    tag = f"wide reduce seed={seed} N={N} T={T} params={n} {dtype} rank={r} {path}"
+    h = zs.zs3_layout_create(N, T, ids, numels)
+    L = oracle.make_layout(N, T, ids, numels)
+    try:
+        S = L.shard_numel
+        n_slots, n_part = zs.zs3_layout_norm_slots(h)
+        # each virtual rank's gradients: only the slice this rank receives is
+        # ever read, so only that slice is drawn (the rest stays zero)
+        grads = []
+        for v in range(N):
+            g = {}
+            for p in L.params:
+                lo, hi = L.own_range(p, r)
+                a = np.zeros(p.numel, np.uint16)
+                if hi > lo:
+                    a[lo:hi] = random_bits16(seed * 101 + v, hi - lo, dtype, 1e-3, 11, p.ds_id)
+                g[p.ds_id] = a
+            grads.append(g)
+        shift = int(rng.integers(0, 8))
+        gflat = Buf16(S, shift=shift, fill=np.full(S, 0x3C3C, np.uint16))
+        partials = torch.full((n_slots,), float("nan"), dtype=torch.float64, device="cuda")
+        ref = np.zeros(S, np.uint16)
+        keep = []
+        pers = [p.ds_id for p in L.params if p.persistent]
+        part = [p.ds_id for p in L.params if not p.persistent]
+        if path == "contiguous" or not part:
+            # slice-only sources: rank v's slices laid out like the flat shard, stride a multiple of 8
+            stride = (S + 7) // 8 * 8
+            host = np.zeros(N * stride, np.uint16)
+            for v in range(N):
+                for p in L.params:
+                    lo, hi = L.own_range(p, r)
+                    host[v * stride + p.shard_offset:v * stride + p.shard_offset + hi - lo] = grads[v][p.ds_id][lo:hi]
+            recv = Buf16(N * stride, shift=shift, fill=host)
+            keep.append(recv)
+            for bi, b in enumerate(oracle.reduce_buckets(L, int(rng.integers(1, sum(numels) + 2)))):
+                oracle.reduce_scatter(L, r, dtype, b, grads, ref)
+                req = [int(x) for x in rng.permutation(b)]
+                src = [recv.ptr() + 2 * (v * stride + L.slot(d).shard_offset) for d in req for v in range(N)]
+                note(f"{tag}: bucket {bi} ({len(b)} params)")
+                zs.zs3_reduce_scatter_local(h, r, dtype, req, src, gflat.ptr(), partials)
+        else:
+            # the chunks each rank sends this rank, each at the address of its
+            # bucket's first grad_flat position modulo 16
+            if pers:
+                oracle.reduce_scatter(L, r, dtype, pers, grads, ref)
+                stride = (S + 7) // 8 * 8
+                host = np.zeros(N * stride, np.uint16)
+                for v in range(N):
+                    for d in pers:
+                        p = L.slot(d)
+                        host[v * stride + p.shard_offset:v * stride + p.shard_offset + p.numel] = grads[v][d]
+                recv = Buf16(N * stride, shift=shift, fill=host)
+                keep.append(recv)
+                src = [recv.ptr() + 2 * (v * stride + L.slot(d).shard_offset) for d in pers for v in range(N)]
+                zs.zs3_reduce_scatter_local(h, r, dtype, pers, src, gflat.ptr(), partials)
+            limit = int(rng.integers(1, sum(L.slot(d).numel for d in part) + 2))
+            for bi, b in enumerate(oracle.gather_buckets(L, limit)):
+                C = sum(L.slot(d).partition_size for d in b)
+                chunks = []          # chunk r of every rank's send buffer (the wire of the pack)
+                for v in range(N):
+                    parts = []
+                    for d in sorted(b):
+                        p = L.slot(d)
+                        lo, hi = L.own_range(p, r)
+                        part = np.zeros(p.partition_size, np.uint16)
+                        part[:hi - lo] = grads[v][d][lo:hi]
+                        parts.append(part)
+                    chunks.append(np.concatenate(parts))
+                oracle.scatter_reduce(L, r, dtype, b, chunks, ref)
+                first = min(L.slot(d).shard_offset for d in b)
+                want = (gflat.ptr() + 2 * first) % 16
+                bufs = []
+                for v in range(N):
+                    buf = Buf16(C + 8, shift=0)
+                    off = ((want - buf.ptr() % 16) % 16) // 2
+                    buf.view[off:off + C].copy_(torch.from_numpy(chunks[v].view(np.int16)).cuda())
+                    bufs.append((buf, buf.ptr() + 2 * off))
+                keep.append(bufs)
+                req = [int(x) for x in rng.permutation(b)]
+                note(f"{tag}: coalesced bucket {bi} ({len(b)} params)")
+                zs.zs3_reduce_scatter_coalesced(h, r, dtype, zs.ZS3_REDUCE, req, recv_chunks=[p for _, p in bufs],
+                                                grad_flat=gflat.ptr(), partials=partials)
+        sync()
+        assert np.array_equal(gflat.host(), ref), "flat gradient"
+        gflat.check_guards()
+        sumsq = torch.zeros(N + 1, dtype=torch.float64, device="cuda")
+        zs.zs3_grad_norm_partials(h, r, partials, sumsq, False)
+        sync()
+        a, q = oracle.grad_norm_partial(L, r, dtype, ref)
+        s = sumsq.cpu().numpy()
+        assert s[r] == pytest.approx(a, rel=1e-12, abs=0), "partitioned sum of squares"
+        assert s[N] == pytest.approx(q, rel=1e-12, abs=0), "persistent sum of squares"
+        del keep
+    finally:
+        zs.zs3_layout_destroy(h)

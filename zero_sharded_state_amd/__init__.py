@@ -45,7 +45,8 @@ EXPORTS = (
     "zs3_abi_version", "zs3_status_str", "zs3_last_error", "zs3_time_next_launch",
     "zs3_layout_create", "zs3_layout_destroy", "zs3_layout_info", "zs3_layout_totals", "zs3_layout_param_at",
     "zs3_layout_param", "zs3_layout_own_range", "zs3_plan_buckets", "zs3_sub_groups",
-    "zs3_bucket_sizes", "zs3_partition", "zs3_gather_coalesced", "zs3_reduce_scatter_local",
+    "zs3_bucket_sizes", "zs3_partition", "zs3_gather_coalesced", "zs3_gather_coalesced_buckets",
+    "zs3_reduce_scatter_local",
     "zs3_layout_norm_slots", "zs3_reduce_scatter_coalesced", "zs3_grad_norm", "zs3_grad_norm_partials",
     "zs3_grad_norm_partials_noalloc",
     "zs3_adam_step", "zs3_adam_step_offload", "zs3_init_master", "zs3_coord_create", "zs3_coord_destroy",
@@ -107,6 +108,8 @@ _SIGNATURES = {
     "zs3_partition": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _p_i64, ctypes.POINTER(_c_p), _c_p, _c_p]),
     "zs3_gather_coalesced": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _p_i64, _c_p, _c_p,
                                       ctypes.POINTER(_c_p), _c_p, _p_i64, _c_p]),
+    "zs3_gather_coalesced_buckets": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _p_i32, _p_i64, _c_p,
+                                              ctypes.POINTER(_c_p), ctypes.POINTER(_c_p), ctypes.POINTER(_c_p), _c_p]),
     "zs3_reduce_scatter_local": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _p_i64, ctypes.POINTER(_c_p),
                                           _c_p, _c_p, _c_p]),
     "zs3_layout_norm_slots": (_c_i32, [_c_p, _p_i64, _p_i64]),
@@ -310,6 +313,21 @@ def zs3_gather_coalesced(layout: int, rank: int, dtype, mode: int, ds_ids: Seque
     _check(lib().zs3_gather_coalesced(layout, rank, _dtype(dtype), mode, n, _i64s(ds_ids), _ptr(shard_flat),
                                       _ptr(own_chunk), chunks, _ptr(full_flat), offs, _stream(stream)))
     return list(offs[:n])
+
+
+def zs3_gather_coalesced_buckets(layout: int, rank: int, dtype, buckets: Sequence[Sequence[int]], shard_flat,
+                                 own_chunks: Sequence, rank_chunks: Sequence[Sequence], full_flats: Sequence,
+                                 stream=None) -> None:
+    """buckets[b] = ds_ids of bucket b; rank_chunks[b] = its N chunk pointers."""
+    starts = [0]
+    flat: List[int] = []
+    for b in buckets:
+        flat += [int(d) for d in b]
+        starts.append(len(flat))
+    chunks = [c for per in rank_chunks for c in per]
+    _check(lib().zs3_gather_coalesced_buckets(layout, rank, _dtype(dtype), len(buckets),
+                                              (ctypes.c_int32 * len(starts))(*starts), _i64s(flat), _ptr(shard_flat),
+                                              _ptrs(own_chunks), _ptrs(chunks), _ptrs(full_flats), _stream(stream)))
 
 
 def zs3_reduce_scatter_local(layout: int, rank: int, dtype, ds_ids: Sequence[int], src: Sequence,

@@ -112,7 +112,7 @@ struct Plan {
 
 enum Op : int64_t {
     kOpPartition = 1, kOpPack, kOpUnpack, kOpReduce, kOpNorm, kOpAdam, kOpGather, kOpScatterPack,
-    kOpScatterReduce, kOpNormSlots, kOpInitMaster
+    kOpScatterReduce, kOpNormSlots, kOpInitMaster, kOpGatherBuckets
 };
 
 constexpr size_t kMaxPlans = 1 << 14;
@@ -383,7 +383,7 @@ zs3_status build_rs_plan(zs3_layout* L, Key&& key, const std::vector<RsSeg>& seg
                 co = false;
         }
     }
-    zs3_status s = check_grid(static_cast<int64_t>(pieces.size()), kRsSub);
+    zs3_status s = check_grid(static_cast<int64_t>(pieces.size()), rs_wide(N, co) ? kRsWideSub : kRsSub);
     if (s != ZS3_OK) return s;
     Plan np;
     np.n_pieces = static_cast<int64_t>(pieces.size());
@@ -525,6 +525,97 @@ zs3_status adam_launch(zs3_layout* L, int32_t rank, int32_t dtype, int64_t begin
                                   static_cast<const uint16_t*>(grad_flat), static_cast<uint16_t*>(shard_flat), scale,
                                   nonfinite, c, vec_ok, static_cast<hipStream_t>(stream)),
                       "Adam kernel launch");
+}
+
+}  // namespace
+
+namespace {
+
+// Chunk offsets c_j (prefix sums of partition sizes) and full offsets f_j
+// (prefix sums of numels) of a bucket, in ascending ds_id; returns the
+// chunk and full sizes.
+void bucket_offsets(const zs3_layout* L, const std::vector<int32_t>& pos, const std::vector<int32_t>& order,
+                    std::vector<int64_t>* c, std::vector<int64_t>* f, int64_t* chunk, int64_t* full) {
+    c->assign(pos.size(), 0);
+    f->assign(pos.size(), 0);
+    int64_t a = 0, b = 0;
+    for (int32_t k : order) {
+        (*c)[k] = a;
+        (*f)[k] = b;
+        a += L->params[pos[k]].ps;
+        b += L->params[pos[k]].numel;
+    }
+    *chunk = a;
+    *full = b;
+}
+
+// The segments of one bucket's fused gather (pack and unpack in one launch,
+// the wire's own slot being the pack's output): the own shard's partitions
+// into the own chunk and, when the two are co-aligned, from the same loads
+// into the own part of each gathered view; then every other rank's chunk
+// into its parts of the views ([codex] 5.2: ds_id order, views of one flat
+// buffer; padding is never unpacked).
+void fused_gather_segments(const zs3_layout* L, int32_t rank, const std::vector<int32_t>& pos,
+                           const std::vector<int32_t>& order, const std::vector<int64_t>& c,
+                           const std::vector<int64_t>& f, const void* shard_flat, void* own_chunk,
+                           const void* const* rank_chunks, void* full_flat, std::vector<CopySeg>* segs) {
+    const int32_t N = L->world;
+    const uint16_t* shard = static_cast<const uint16_t*>(shard_flat);
+    uint16_t* own = static_cast<uint16_t*>(own_chunk);
+    uint16_t* dst = static_cast<uint16_t*>(full_flat);
+    for (int32_t k : order) {
+        const Slot& p = L->params[pos[k]];
+        int64_t lo, hi;
+        p.own_range(rank, &lo, &hi);
+        uint16_t* own_dst = own + c[k];
+        uint16_t* full_dst = dst + f[k] + lo;
+        // read the own shard once for both destinations when they are co-aligned
+        const bool both = hi > lo && ((reinterpret_cast<uintptr_t>(own_dst) ^ reinterpret_cast<uintptr_t>(full_dst)) & 15u) == 0;
+        if (both) {
+            segs->push_back(CopySeg{shard + p.offset, own_dst, p.ps, full_dst, hi - lo});
+        } else {
+            segs->push_back(CopySeg{shard + p.offset, own_dst, p.ps, nullptr, 0});
+            segs->push_back(CopySeg{shard + p.offset, full_dst, hi - lo, nullptr, 0});
+        }
+    }
+    for (int32_t k : order) {
+        const Slot& p = L->params[pos[k]];
+        for (int32_t v = 0; v < N; ++v) {
+            if (v == rank) continue;
+            int64_t lo, hi;
+            p.own_range(v, &lo, &hi);
+            segs->push_back(CopySeg{static_cast<const uint16_t*>(rank_chunks[v]) + c[k], dst + f[k] + lo, hi - lo,
+                                    nullptr, 0});
+        }
+    }
+}
+
+// Byte ranges a call writes and reads: no written range may overlap another
+// range (sort and sweep, O(k log k) for calls over many buffers).
+struct Range {
+    uintptr_t lo, hi;
+    bool write;
+    int32_t tag;
+};
+
+const Range* first_overlap(std::vector<Range>* rs, const Range** other) {
+    std::sort(rs->begin(), rs->end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+    const Range* max_any = nullptr;      // range with the largest end so far
+    const Range* max_write = nullptr;    // written range with the largest end so far
+    for (const Range& r : *rs) {
+        if (r.hi <= r.lo) continue;
+        if (r.write && max_any != nullptr && r.lo < max_any->hi) {
+            *other = max_any;
+            return &r;
+        }
+        if (!r.write && max_write != nullptr && r.lo < max_write->hi) {
+            *other = max_write;
+            return &r;
+        }
+        if (max_any == nullptr || r.hi > max_any->hi) max_any = &r;
+        if (r.write && (max_write == nullptr || r.hi > max_write->hi)) max_write = &r;
+    }
+    return nullptr;
 }
 
 }  // namespace
@@ -791,14 +882,9 @@ zs3_status zs3_gather_coalesced(zs3_layout_t L, int32_t rank, int32_t dtype, int
     if ((s = resolve(L, n, ds_ids, false, &pos, &order)) != ZS3_OK) return s;
     const int32_t N = L->world;
     // chunk offsets c_j and full offsets f_j in ascending ds_id
-    std::vector<int64_t> c(n), f(n);
-    int64_t chunk = 0, full = 0;
-    for (int32_t k : order) {
-        c[k] = chunk;
-        f[k] = full;
-        chunk += L->params[pos[k]].ps;
-        full += L->params[pos[k]].numel;
-    }
+    std::vector<int64_t> c, f;
+    int64_t chunk, full;
+    bucket_offsets(L, pos, order, &c, &f, &chunk, &full);
     const bool do_pack = (mode & ZS3_PACK) != 0, do_unpack = (mode & ZS3_UNPACK) != 0;
     if (do_pack) {
         if ((s = check_ptr16(shard_flat, "shard_flat")) != ZS3_OK) return s;
@@ -832,34 +918,7 @@ zs3_status zs3_gather_coalesced(zs3_layout_t L, int32_t rank, int32_t dtype, int
         Plan* plan = find_plan(L, key);
         if (plan == nullptr) {
             std::vector<CopySeg> segs;
-            const uint16_t* shard = static_cast<const uint16_t*>(shard_flat);
-            uint16_t* own = static_cast<uint16_t*>(own_chunk);
-            uint16_t* dst = static_cast<uint16_t*>(full_flat);
-            for (int32_t k : order) {
-                const Slot& p = L->params[pos[k]];
-                int64_t lo, hi;
-                p.own_range(rank, &lo, &hi);
-                uint16_t* own_dst = own + c[k];
-                uint16_t* full_dst = dst + f[k] + lo;
-                // read the own shard once for both destinations when they are co-aligned
-                const bool both = hi > lo && ((reinterpret_cast<uintptr_t>(own_dst) ^ reinterpret_cast<uintptr_t>(full_dst)) & 15u) == 0;
-                if (both) {
-                    segs.push_back(CopySeg{shard + p.offset, own_dst, p.ps, full_dst, hi - lo});
-                } else {
-                    segs.push_back(CopySeg{shard + p.offset, own_dst, p.ps, nullptr, 0});
-                    segs.push_back(CopySeg{shard + p.offset, full_dst, hi - lo, nullptr, 0});
-                }
-            }
-            for (int32_t k : order) {
-                const Slot& p = L->params[pos[k]];
-                for (int32_t v = 0; v < N; ++v) {
-                    if (v == rank) continue;
-                    int64_t lo, hi;
-                    p.own_range(v, &lo, &hi);
-                    segs.push_back(CopySeg{static_cast<const uint16_t*>(rank_chunks[v]) + c[k], dst + f[k] + lo, hi - lo,
-                                           nullptr, 0});
-                }
-            }
+            fused_gather_segments(L, rank, pos, order, c, f, shard_flat, own_chunk, rank_chunks, full_flat, &segs);
             if ((s = build_copy_plan(L, std::move(key), segs, &plan)) != ZS3_OK) return s;
         }
         return run_copy(kCopyGather, plan, stream);
@@ -903,6 +962,75 @@ zs3_status zs3_gather_coalesced(zs3_layout_t L, int32_t rank, int32_t dtype, int
         if ((s = run_copy(kCopyUnpack, plan, stream)) != ZS3_OK) return s;
     }
     return ok();
+}
+
+zs3_status zs3_gather_coalesced_buckets(zs3_layout_t L, int32_t rank, int32_t dtype, int32_t n_buckets,
+                                        const int32_t* bucket_start, const int64_t* ds_ids, const void* shard_flat,
+                                        void* const* own_chunks, const void* const* rank_chunks,
+                                        void* const* full_flats, void* stream) {
+    zs3_status s = check_layout_rank(L, rank);
+    if (s != ZS3_OK) return s;
+    if ((s = check_dtype(dtype)) != ZS3_OK) return s;
+    if (n_buckets < 0) return fail(ZS3_EINVAL, "n_buckets = %d < 0", n_buckets);
+    if (n_buckets == 0) return ok();
+    if (bucket_start == nullptr || own_chunks == nullptr || rank_chunks == nullptr || full_flats == nullptr)
+        return fail(ZS3_EINVAL, "bucket_start, own_chunks, rank_chunks or full_flats is NULL");
+    if (bucket_start[0] != 0) return fail(ZS3_EINVAL, "bucket_start[0] = %d, not 0", bucket_start[0]);
+    if ((s = check_ptr16(shard_flat, "shard_flat")) != ZS3_OK) return s;
+    const int32_t N = L->world;
+    std::vector<Range> ranges;
+    ranges.push_back(Range{reinterpret_cast<uintptr_t>(shard_flat),
+                           reinterpret_cast<uintptr_t>(shard_flat) + 2 * static_cast<uintptr_t>(L->shard_numel), false, -1});
+    struct B {
+        std::vector<int32_t> pos, order;
+        std::vector<int64_t> c, f;
+    };
+    std::vector<B> bk(n_buckets);
+    std::unordered_set<int64_t> seen;
+    for (int32_t b = 0; b < n_buckets; ++b) {
+        const int32_t a = bucket_start[b], e = bucket_start[b + 1];
+        if (e <= a) return fail(ZS3_EINVAL, "bucket %d is empty or bucket_start is not increasing", b);
+        if ((s = resolve(L, e - a, ds_ids + a, false, &bk[b].pos, &bk[b].order)) != ZS3_OK) return s;
+        for (int32_t i = a; i < e; ++i)
+            if (!seen.insert(ds_ids[i]).second) return fail(ZS3_EDUPID, "ds_id %lld in two buckets", (long long)ds_ids[i]);
+        int64_t chunk, full;
+        bucket_offsets(L, bk[b].pos, bk[b].order, &bk[b].c, &bk[b].f, &chunk, &full);
+        if ((s = check_ptr16(own_chunks[b], "own_chunks[b]")) != ZS3_OK) return s;
+        if ((s = check_ptr16(full_flats[b], "full_flats[b]")) != ZS3_OK) return s;
+        if (rank_chunks[static_cast<int64_t>(b) * N + rank] != own_chunks[b])
+            return fail(ZS3_EINVAL, "rank_chunks[%d*N + rank] is not own_chunks[%d]", b, b);
+        const uintptr_t oc = reinterpret_cast<uintptr_t>(own_chunks[b]), ff = reinterpret_cast<uintptr_t>(full_flats[b]);
+        ranges.push_back(Range{oc, oc + 2 * static_cast<uintptr_t>(chunk), true, b});
+        ranges.push_back(Range{ff, ff + 2 * static_cast<uintptr_t>(full), true, b});
+        for (int32_t v = 0; v < N; ++v) {
+            if (v == rank) continue;
+            const void* q = rank_chunks[static_cast<int64_t>(b) * N + v];
+            if ((s = check_ptr16(q, "rank_chunks[b*N+v]")) != ZS3_OK) return s;
+            const uintptr_t x = reinterpret_cast<uintptr_t>(q);
+            ranges.push_back(Range{x, x + 2 * static_cast<uintptr_t>(chunk), false, b});
+        }
+    }
+    const Range* other = nullptr;
+    if (const Range* bad = first_overlap(&ranges, &other))
+        return fail(ZS3_EALIAS, "an output of bucket %d overlaps a buffer of bucket %d", bad->write ? bad->tag : other->tag,
+                    bad->write ? other->tag : bad->tag);
+
+    Key key{{kOpGatherBuckets, device_id(), rank, reinterpret_cast<int64_t>(shard_flat), n_buckets}};
+    for (int32_t b = 0; b < n_buckets; ++b) {
+        key.w.push_back(bucket_start[b + 1]);
+        key.w.push_back(reinterpret_cast<int64_t>(full_flats[b]));
+        for (int32_t v = 0; v < N; ++v) key.w.push_back(reinterpret_cast<int64_t>(rank_chunks[static_cast<int64_t>(b) * N + v]));
+        for (int32_t k : bk[b].order) key.w.push_back(L->params[bk[b].pos[k]].ds_id);
+    }
+    Plan* plan = find_plan(L, key);
+    if (plan == nullptr) {
+        std::vector<CopySeg> segs;
+        for (int32_t b = 0; b < n_buckets; ++b)
+            fused_gather_segments(L, rank, bk[b].pos, bk[b].order, bk[b].c, bk[b].f, shard_flat, own_chunks[b],
+                                  rank_chunks + static_cast<int64_t>(b) * N, full_flats[b], &segs);
+        if ((s = build_copy_plan(L, std::move(key), segs, &plan)) != ZS3_OK) return s;
+    }
+    return run_copy(kCopyGather, plan, stream);
 }
 
 // ---------------------------------------------------------------- (3)

@@ -569,6 +569,122 @@ __device__ __forceinline__ double rs_piece(const SRC& sp, uint16_t* seg_dst, int
     return ss;
 }
 
+// ------------------------------------------ wide reduce-scatter (large N)
+// With many ranks, every output element reads N sources: the kernel above
+// then makes N/kRsBatch dependent rounds of loads per workgroup, and a
+// bucket's slice fills few workgroups (a c5-sized bucket at N = 64: ~130).
+// Here a piece is shared by kRsWideSub workgroups of 1024 elements; a
+// thread holds 4 consecutive elements, reads them with one 8-byte load per
+// source, and keeps kRsWideBatch sources' loads in flight, so a workgroup
+// makes N/kRsWideBatch rounds and a bucket fills 4x the workgroups.  Each
+// element's N adds still run in rank order (bit-identical results).  Used
+// when every source is co-aligned with its destination modulo 16 bytes.
+
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+// 8 bytes (4 elements) at an 8-byte aligned address.
+__device__ __forceinline__ void ld8(const uint16_t* p, uint32_t (&x)[2]) {
+    v2u v;
+    if constexpr (kNtRs) v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+    else v = *reinterpret_cast<const v2u*>(p);
+    x[0] = v.x;
+    x[1] = v.y;
+}
+
+// `count` (<= 4) consecutive destination elements starting at slice
+// position k, the first clamp(real - k, 0, count) of them real: their
+// sources read with 2-byte loads, kRsWideTailBatch sources in flight.
+template <int D, bool NORM, class SRC>
+__device__ __forceinline__ void rs_wide_group(uint16_t* dst, const SRC& sp, int world, Divider div, int64_t k,
+                                              int64_t real, int count, double& ss) {
+    int64_t ne = real - k;
+    if (ne < 0) ne = 0;
+    if (ne > count) ne = count;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (ne > 0) {
+        for (int vb = 0; vb < world; vb += kRsWideTailBatch) {
+            uint32_t x[kRsWideTailBatch][4];
+#pragma unroll
+            for (int j = 0; j < kRsWideTailBatch; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (vb + j < world && e < ne) x[j][e] = sp(vb + j)[k + e];
+#pragma unroll
+            for (int j = 0; j < kRsWideTailBatch; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (vb + j < world && e < ne) acc[e] += widen<D>(x[j][e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (e < count) {
+            const uint16_t x = e < ne ? static_cast<uint16_t>(narrow<D>(div(acc[e]))) : uint16_t(0);
+            dst[e] = x;
+            if constexpr (NORM) ss += sq_fast<D>(x);
+        }
+    }
+}
+
+// Returns the thread's sum of squares of the values it wrote (0 unless NORM).
+template <int D, bool NORM, class SRC>
+__device__ __forceinline__ double rs_piece_wide(const SRC& sp, uint16_t* seg_dst, int64_t real, int64_t begin,
+                                                int64_t len, int world, Divider div, int sub, int t) {
+    double ss = 0.0;
+    int64_t k0 = begin;
+    int64_t n = len;
+    uint16_t* dst = seg_dst + k0;
+    int64_t h = head16(dst);
+    if (h > n) h = n;
+    // the head (< 8 elements, until dst is 16-byte aligned): two groups of 4
+    if (sub == 0 && t < 2 && 4 * t < h) {
+        const int c = static_cast<int>(h - 4 * t < 4 ? h - 4 * t : 4);
+        rs_wide_group<D, NORM>(dst + 4 * t, sp, world, div, k0 + 4 * t, real, c, ss);
+    }
+    k0 += h;
+    dst += h;
+    n -= h;
+    const int64_t nq = n >> 2;                                // groups of 4 (8 bytes)
+    int64_t nfull = real > k0 ? (real - k0) >> 2 : 0;
+    if (nfull > nq) nfull = nq;
+    const int64_t i = int64_t(sub) * kBlock + t;              // this thread's group
+    if (i < nfull) {
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int vb = 0; vb < world; vb += kRsWideBatch) {
+            uint32_t x[kRsWideBatch][2];
+#pragma unroll
+            for (int j = 0; j < kRsWideBatch; ++j)
+                if (vb + j < world) ld8(sp(vb + j) + k0 + 4 * i, x[j]);
+#pragma unroll
+            for (int j = 0; j < kRsWideBatch; ++j) {
+                if (vb + j < world) {
+                    acc[0] += widen<D>(lo16(x[j][0]));
+                    acc[1] += widen<D>(hi16(x[j][0]));
+                    acc[2] += widen<D>(lo16(x[j][1]));
+                    acc[3] += widen<D>(hi16(x[j][1]));
+                }
+            }
+        }
+        uint32_t b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            b[e] = narrow<D>(div(acc[e]));
+            if constexpr (NORM) ss += sq_fast<D>(b[e]);
+        }
+        const v2u o = {pack2(b[0], b[1]), pack2(b[2], b[3])};
+        v2u* q = reinterpret_cast<v2u*>(dst + 4 * i);
+        if constexpr (kNtRs) __builtin_nontemporal_store(o, q);
+        else *q = o;
+    } else if (i < nq) {
+        // the group holding the slice's real end, or padding past it
+        rs_wide_group<D, NORM>(dst + 4 * i, sp, world, div, k0 + 4 * i, real, 4, ss);
+    }
+    const int64_t rem = n & 3;
+    if (sub == kRsWideSub - 1 && t == 0 && rem > 0)
+        rs_wide_group<D, NORM>(dst + 4 * nq, sp, world, div, k0 + 4 * nq, real, static_cast<int>(rem), ss);
+    return ss;
+}
+
 // Pieces of a slice of `total` elements whose destination needs `head`
 // elements to reach 16-byte alignment (the host's split), and the index of
 // the piece that starts at `begin`.
@@ -604,6 +720,54 @@ __device__ __forceinline__ void put_partial(double ss, double* partials, int64_t
             if (spare) partials[at + kNormSlotsPerGroup] = 0.0;
         }
     }
+}
+
+// Wide kernel: workgroup `sub` of piece q writes one slot, its workgroup sum
+// (kRsWideSub workgroups per piece fill the group's kNormSlotsPerGroup slots).
+__device__ __forceinline__ void put_partial_wide(double ss, double* partials, int64_t slot, int64_t q, int64_t actual,
+                                                 int64_t total, int sub, double* sh) {
+    const bool spare = q == actual - 1 && actual < norm_slot_groups(total);
+    const double s = block_sum(ss, sh);
+    if (threadIdx.x == 0) {
+        const int64_t at = slot + q * kNormSlotsPerGroup + sub;
+        partials[at] = s;
+        if (spare) partials[at + kNormSlotsPerGroup] = 0.0;
+    }
+}
+
+template <int D, bool NORM>
+__device__ __forceinline__ void rs_table_wide(const RsSeg* __restrict__ segs, const Piece* __restrict__ pieces,
+                                              const uint16_t* const* __restrict__ srcs, int world, Divider div,
+                                              double* __restrict__ partials) {
+    __shared__ double sh[kBlock / 64];
+    const uint32_t pidx = blockIdx.x / kRsWideSub;
+    const int sub = static_cast<int>(blockIdx.x % kRsWideSub);
+    const Piece pc = pieces[pidx];
+    const RsSeg sg = segs[pc.seg];
+    const TableSrcs sp{srcs + sg.src_index};
+    const double ss = rs_piece_wide<D, NORM>(sp, sg.dst, sg.real, pc.begin, pc.len, world, div, sub, threadIdx.x);
+    if constexpr (NORM) {
+        const int64_t head = head16(sg.dst);
+        put_partial_wide(ss, partials, sg.slot, piece_index(pc.begin, head), pieces_of(sg.total, head), sg.total, sub,
+                         sh);
+    }
+}
+
+template <int D, bool NORM>
+__device__ __forceinline__ void rs_inline_wide(const RsInline& plan, Divider div, double* __restrict__ partials) {
+    __shared__ double sh[kBlock / 64];
+    const int32_t pidx = static_cast<int32_t>(blockIdx.x / kRsWideSub);
+    const int sub = static_cast<int>(blockIdx.x % kRsWideSub);
+    const int s = find_seg<kRsInlineSegs>(plan.piece_start, plan.nseg, pidx);
+    const int64_t q = pidx - plan.piece_start[s];
+    int64_t begin, len;
+    piece_range(q, plan.total[s], plan.head[s], kRsPiece, &begin, &len);
+    const InlineSrcs sp{plan, s * plan.world};
+    const double ss = rs_piece_wide<D, NORM>(sp, plan.dst[s], plan.real[s], begin, len, plan.world, div, sub,
+                                             threadIdx.x);
+    if constexpr (NORM)
+        put_partial_wide(ss, partials, plan.slot[s], q, plan.piece_start[s + 1] - plan.piece_start[s], plan.total[s],
+                         sub, sh);
 }
 
 template <int D, bool ALIGNED, bool NORM>
@@ -669,6 +833,35 @@ template <int D, bool ALIGNED, bool NORM>
 __global__ __launch_bounds__(kBlock) void k_scatter_reduce_inline(const RsInline plan, Divider div,
                                                                   double* __restrict__ partials) {
     rs_inline<D, ALIGNED, NORM>(plan, div, partials);
+}
+
+// Wide forms (many ranks, co-aligned sources), same two names per path.
+template <int D, bool NORM>
+__global__ __launch_bounds__(kBlock) void k_reduce_scatter_wide(const RsSeg* __restrict__ segs,
+                                                                const Piece* __restrict__ pieces,
+                                                                const uint16_t* const* __restrict__ srcs, int world,
+                                                                Divider div, double* __restrict__ partials) {
+    rs_table_wide<D, NORM>(segs, pieces, srcs, world, div, partials);
+}
+
+template <int D, bool NORM>
+__global__ __launch_bounds__(kBlock) void k_reduce_scatter_wide_inline(const RsInline plan, Divider div,
+                                                                       double* __restrict__ partials) {
+    rs_inline_wide<D, NORM>(plan, div, partials);
+}
+
+template <int D, bool NORM>
+__global__ __launch_bounds__(kBlock) void k_scatter_reduce_wide(const RsSeg* __restrict__ segs,
+                                                                const Piece* __restrict__ pieces,
+                                                                const uint16_t* const* __restrict__ srcs, int world,
+                                                                Divider div, double* __restrict__ partials) {
+    rs_table_wide<D, NORM>(segs, pieces, srcs, world, div, partials);
+}
+
+template <int D, bool NORM>
+__global__ __launch_bounds__(kBlock) void k_scatter_reduce_wide_inline(const RsInline plan, Divider div,
+                                                                       double* __restrict__ partials) {
+    rs_inline_wide<D, NORM>(plan, div, partials);
 }
 
 // ------------------------------------------------------------ grad norm
@@ -1031,6 +1224,24 @@ void rs_launch_inline(RsPath path, dim3 g, hipStream_t stream, const RsInline& p
         launch((k_reduce_scatter_inline<D, A, NORM>), g, dim3(kBlock), stream, plan, div, partials);
 }
 
+template <int D, bool NORM>
+void rs_launch_table_wide(RsPath path, dim3 g, hipStream_t stream, const RsSeg* segs, const Piece* pieces,
+                          const uint16_t* const* srcs, int32_t world, Divider div, double* partials) {
+    if (path == kRsCoalesced)
+        launch((k_scatter_reduce_wide<D, NORM>), g, dim3(kBlock), stream, segs, pieces, srcs, world, div, partials);
+    else
+        launch((k_reduce_scatter_wide<D, NORM>), g, dim3(kBlock), stream, segs, pieces, srcs, world, div, partials);
+}
+
+template <int D, bool NORM>
+void rs_launch_inline_wide(RsPath path, dim3 g, hipStream_t stream, const RsInline& plan, Divider div,
+                           double* partials) {
+    if (path == kRsCoalesced)
+        launch((k_scatter_reduce_wide_inline<D, NORM>), g, dim3(kBlock), stream, plan, div, partials);
+    else
+        launch((k_reduce_scatter_wide_inline<D, NORM>), g, dim3(kBlock), stream, plan, div, partials);
+}
+
 template <int D>
 void rs_dispatch_table(RsPath path, bool co, bool norm, dim3 g, hipStream_t stream, const RsSeg* segs,
                        const Piece* pieces, const uint16_t* const* srcs, int32_t world, Divider div,
@@ -1061,8 +1272,19 @@ hipError_t launch_reduce_scatter(RsPath path, int32_t dtype, const RsSeg* segs, 
                                  double* partials, hipStream_t stream) {
     if (n_pieces <= 0) return hipSuccess;
     const Divider div = make_divider(world);
-    const dim3 g = grid_of(n_pieces * kRsSub);
     const bool norm = partials != nullptr;
+    if (rs_wide(world, co_aligned)) {
+        const dim3 g = grid_of(n_pieces * kRsWideSub);
+        if (dtype == kFP16) {
+            if (norm) rs_launch_table_wide<kFP16, true>(path, g, stream, segs, pieces, srcs, world, div, partials);
+            else rs_launch_table_wide<kFP16, false>(path, g, stream, segs, pieces, srcs, world, div, partials);
+        } else {
+            if (norm) rs_launch_table_wide<kBF16, true>(path, g, stream, segs, pieces, srcs, world, div, partials);
+            else rs_launch_table_wide<kBF16, false>(path, g, stream, segs, pieces, srcs, world, div, partials);
+        }
+        return hipGetLastError();
+    }
+    const dim3 g = grid_of(n_pieces * kRsSub);
     if (dtype == kFP16) rs_dispatch_table<kFP16>(path, co_aligned, norm, g, stream, segs, pieces, srcs, world, div, partials);
     else rs_dispatch_table<kBF16>(path, co_aligned, norm, g, stream, segs, pieces, srcs, world, div, partials);
     return hipGetLastError();
@@ -1073,8 +1295,19 @@ hipError_t launch_reduce_scatter_inline(RsPath path, int32_t dtype, const RsInli
     const int64_t n_pieces = plan.piece_start[plan.nseg];
     if (n_pieces <= 0) return hipSuccess;
     const Divider div = make_divider(plan.world);
-    const dim3 g = grid_of(n_pieces * kRsSub);
     const bool norm = partials != nullptr;
+    if (rs_wide(plan.world, co_aligned)) {
+        const dim3 g = grid_of(n_pieces * kRsWideSub);
+        if (dtype == kFP16) {
+            if (norm) rs_launch_inline_wide<kFP16, true>(path, g, stream, plan, div, partials);
+            else rs_launch_inline_wide<kFP16, false>(path, g, stream, plan, div, partials);
+        } else {
+            if (norm) rs_launch_inline_wide<kBF16, true>(path, g, stream, plan, div, partials);
+            else rs_launch_inline_wide<kBF16, false>(path, g, stream, plan, div, partials);
+        }
+        return hipGetLastError();
+    }
+    const dim3 g = grid_of(n_pieces * kRsSub);
     if (dtype == kFP16) rs_dispatch_inline<kFP16>(path, co_aligned, norm, g, stream, plan, div, partials);
     else rs_dispatch_inline<kBF16>(path, co_aligned, norm, g, stream, plan, div, partials);
     return hipGetLastError();

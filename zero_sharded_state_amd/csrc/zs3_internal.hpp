@@ -124,6 +124,23 @@ __host__ __device__ constexpr int64_t norm_slot_groups(int64_t total) {
     return total <= kRsPiece ? 1 : (total + kRsPiece - 1) / kRsPiece;
 }
 
+// The wide reduce-scatter (many ranks): kRsWideSub workgroups of kBlock
+// threads x 4 elements share a piece, one norm slot each; kRsWideBatch
+// sources' loads in flight per round (kRsWideTailBatch for the ragged ends).
+#ifndef ZS3_RS_WIDE_MIN
+#define ZS3_RS_WIDE_MIN 16
+#endif
+#ifndef ZS3_RS_WIDE_BATCH
+#define ZS3_RS_WIDE_BATCH 32
+#endif
+constexpr int kRsWideMin = ZS3_RS_WIDE_MIN;          // world sizes from which the wide kernel runs
+constexpr int kRsWideBatch = ZS3_RS_WIDE_BATCH;
+constexpr int kRsWideTailBatch = 16;
+constexpr int kRsWideSub = static_cast<int>(kRsPiece / (int64_t(kBlock) * 4));
+static_assert(kRsWideSub * int64_t(kBlock) * 4 == kRsPiece, "a piece must split into whole wide workgroups");
+static_assert(kRsWideSub == kNormSlotsPerGroup, "one norm slot per wide workgroup");
+inline bool rs_wide(int32_t world, bool co_aligned) { return co_aligned && world >= kRsWideMin; }
+
 // Calls with few segments carry their whole plan in the kernel arguments
 // (structure of arrays, < 2 KB each): the workgroup finds its segment from
 // the prefix of piece counts and computes its range, with no loads before

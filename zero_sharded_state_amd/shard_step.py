@@ -59,11 +59,28 @@ class ShardStep:
                  sub_group_size: int, adam: AdamConfig = AdamConfig(), max_norm: float = 1.0,
                  device: str = "cuda", rs_streams: int = 1, gather_streams: int = 1,
                  fuse_norm: bool = False, reduce_path: str = "contiguous", offload: bool = False,
-                 offload_chunk: int = 0):
+                 offload_chunk: int = 0, recv_layout: str = "rank", single_launch="none"):
         import torch
 
         if reduce_path not in ("contiguous", "coalesced"):
             raise ValueError(f"reduce_path {reduce_path!r} is not 'contiguous' or 'coalesced'")
+        if recv_layout not in ("rank", "bucket"):
+            raise ValueError(f"recv_layout {recv_layout!r} is not 'rank' or 'bucket'")
+        self.recv_layout = recv_layout
+        # single_launch "gather": each gather pass is one launch over every
+        # bucket (each bucket keeps its own wire and gathered buffer);
+        # "reduce": the gradient phase is one launch over every bucket's
+        # parameters; "both", or "none" (one launch per bucket).  The
+        # results are those of the per-bucket calls, bit for bit.
+        if single_launch is True or single_launch is False:
+            single_launch = "both" if single_launch else "none"
+        if single_launch not in ("none", "gather", "reduce", "both"):
+            raise ValueError(f"single_launch {single_launch!r} is not none, gather, reduce or both")
+        self.single_gather = single_launch in ("gather", "both")
+        self.single_reduce = single_launch in ("reduce", "both")
+        if self.single_reduce and reduce_path != "contiguous":
+            raise ValueError("a single-launch gradient phase needs the contiguous gradient path")
+        self.single_launch = single_launch
         self.fuse_norm = bool(fuse_norm)
         self.reduce_path = reduce_path
 
@@ -121,12 +138,29 @@ class ShardStep:
         self.wire = torch.empty(max(1, self.W), dtype=i16, device=dev)        # per-bucket all-gather output
         self.shard = torch.zeros(max(1, self.S), dtype=i16, device=dev)
         self.grad = torch.zeros(max(1, self.S), dtype=i16, device=dev)
-        # the slices the N ranks send this rank, laid out like the flat shard,
-        # one per rank at a stride rounded up to 8 elements: every source of
-        # an element then has the byte address of its grad_flat destination
-        # modulo 16 (the reduce-scatter's co-aligned 128-bit path)
+        # The slices the N ranks send this rank.  "rank": one copy of the
+        # flat shard's layout per rank, at a stride rounded up to 8 elements.
+        # "bucket": per gradient bucket, its N slices next to each other
+        # (what an all-to-all of the bucket delivers), so the sources of one
+        # element lie within one bucket's region.  Either way every source
+        # of an element has the byte address of its grad_flat destination
+        # modulo 16 (the reduce-scatter's co-aligned 128-bit path).
         self.recv_stride = (self.S + 7) // 8 * 8
-        self.recv = torch.zeros(max(1, self.N * self.recv_stride), dtype=i16, device=dev)
+        self._recv_region: Dict[int, Tuple[int, int, int]] = {}    # ds_id -> (base, stride, lo) of its bucket
+        if recv_layout == "rank":
+            recv_len = self.N * self.recv_stride
+        else:
+            cur = 0
+            for b in self.reduce_buckets:
+                lo = min(self.by_id[d]["shard_offset"] for d in b)
+                hi = max(self.by_id[d]["shard_offset"] + self.by_id[d]["partition_size"] for d in b)
+                stride = (hi - lo + 7) // 8 * 8
+                base = cur + (lo - cur) % 8               # base = lo (mod 8): co-aligned with grad_flat
+                for d in b:
+                    self._recv_region[d] = (base, stride, lo)
+                cur = base + self.N * stride
+            recv_len = cur
+        self.recv = torch.zeros(max(1, recv_len), dtype=i16, device=dev)
         # the fp32 optimizer partition (master, momentum, variance) is one
         # allocation, each array starting on a 2 MiB boundary; offloaded, it
         # lives in pinned host memory ([codex] 6.1, 6.3)
@@ -176,9 +210,18 @@ class ShardStep:
         _, _, w, c = self.bucket_meta[bucket]
         return self.wire.data_ptr() + 2 * (w + v * c)
 
+    def recv_index(self, v: int, ds_id: int) -> int:
+        """Element offset in ``recv`` of virtual rank v's slice of parameter
+        ds_id for this rank."""
+        off = self.by_id[ds_id]["shard_offset"]
+        if self.recv_layout == "rank":
+            return v * self.recv_stride + off
+        base, stride, lo = self._recv_region[ds_id]
+        return base + v * stride + (off - lo)
+
     def recv_ptr(self, v: int, ds_id: int) -> int:
         """Where virtual rank v's slice of parameter ds_id for this rank lives."""
-        return self.recv.data_ptr() + 2 * (v * self.recv_stride + self.by_id[ds_id]["shard_offset"])
+        return self.recv.data_ptr() + 2 * self.recv_index(v, ds_id)
 
     def _coalesced_buffers(self):
         """Own full gradients, per-bucket send buffers and received chunks.
@@ -273,6 +316,20 @@ class ShardStep:
         all_ids = [p["ds_id"] for p in self.params]
         self._p = (len(all_ids), (I64 * len(all_ids))(*all_ids),
                    (P * len(all_ids))(*[self.full_param_ptr(d) for d in all_ids]))
+        if self.single_gather:
+            nb = len(self.gather_buckets)
+            starts, flat = [0], []
+            for b in self.gather_buckets:
+                flat += b
+                starts.append(len(flat))
+            self._gm = (nb, (ctypes.c_int32 * (nb + 1))(*starts), (I64 * max(1, len(flat)))(*flat),
+                        (P * max(1, nb))(*[self._g[bi][2] for bi in range(nb)]),
+                        (P * max(1, nb * self.N))(*[self.chunk_ptr(bi, v) for bi in range(nb) for v in range(self.N)]),
+                        (P * max(1, nb))(*[self._g[bi][4] for bi in range(nb)]))
+        if self.single_reduce:
+            rs_ids = [d for b in self.reduce_buckets for d in b]
+            self._rm = (len(rs_ids), (I64 * len(rs_ids))(*rs_ids),
+                        (P * (len(rs_ids) * self.N))(*[self.recv_ptr(v, d) for d in rs_ids for v in range(self.N)]))
 
     # ------------------------------------------------------------- phases
     def _stream(self) -> int:
@@ -317,13 +374,22 @@ class ShardStep:
             e.record(a)
             main.wait_event(e)
 
-    def gather_pass(self, stream=None, timer=None):
+    def gather_pass(self, stream=None, timer=None, streams=None):
         """Every gather bucket; buckets are independent, so with several
-        gather streams they are dealt round-robin and joined at the end.
+        gather streams they are dealt round-robin and joined at the end
+        (``streams`` overrides the step's count for this pass).
         ``timer()``, if given, returns a (start, stop) hipEvent_t pair that
         the bucket's kernel records its own start and end into."""
-        main, aux, handles = self._fanout(stream, self.gather_streams)
         lib = zs.lib()
+        if self.single_gather:
+            nb, starts, ids, owns, chunks, fulls = self._gm
+            if timer is not None:
+                lib.zs3_time_next_launch(*timer())
+            self._ok(lib.zs3_gather_coalesced_buckets(self.h, self.rank, self.dcode, nb, starts, ids,
+                                                      self.shard.data_ptr(), owns, chunks, fulls,
+                                                      stream if stream is not None else self._stream()))
+            return
+        main, aux, handles = self._fanout(stream, self.gather_streams if streams is None else streams)
         for bi in range(len(self._g)):
             if timer is not None:
                 lib.zs3_time_next_launch(*timer())
@@ -333,9 +399,14 @@ class ShardStep:
     def reduce_scatter(self, stream=None):
         """Every gradient bucket, fanned out over the main and auxiliary
         streams and joined back into the main stream."""
-        main, aux, handles = self._fanout(stream, self.rs_streams)
         lib = zs.lib()
         partials = self.partials.data_ptr() if self.fuse_norm else None
+        if self.single_reduce:
+            n, ids, src = self._rm
+            self._ok(lib.zs3_reduce_scatter_local(self.h, self.rank, self.dcode, n, ids, src, self.grad.data_ptr(),
+                                                  partials, stream if stream is not None else self._stream()))
+            return
+        main, aux, handles = self._fanout(stream, self.rs_streams)
         for i, (n, ids, grads, send, recv) in enumerate(self._x):
             self._ok(lib.zs3_reduce_scatter_coalesced(self.h, self.rank, self.dcode, zs.ZS3_PACK | zs.ZS3_REDUCE,
                                                       n, ids, grads, send, recv, self.grad.data_ptr(), partials,
