@@ -92,23 +92,14 @@ __device__ __forceinline__ void st_stream(void* p, v4u v) {
 // than the Infinity Cache this measured 1.3% faster gathers than the plain
 // non-temporal store (and slower reduce-scatter stores, which keep that).
 // A vector store of ordinary data to a valid address; only the caching
-// hint differs.
+// hint differs.  The compiler cannot see that this asm is a store, so it
+// does not keep the wait states a store of more than 8 bytes needs before
+// a VALU instruction may overwrite its data registers (two on this GPU
+// family): the s_nop 1 inside the block provides them, whatever the
+// compiler schedules next.
 __device__ __forceinline__ void st_copy(void* p, v4u v) {
     v4u* q = reinterpret_cast<v4u*>(p);
-    if constexpr (kNtCopy) asm volatile("global_store_dwordx4 %0, %1, off nt sc1" ::"v"(q), "v"(v) : "memory");
-    else *q = v;
-}
-
-template <bool NT>
-__device__ __forceinline__ v4f ld_stream_f(const float* p) {
-    const v4f* q = reinterpret_cast<const v4f*>(p);
-    if constexpr (NT) return __builtin_nontemporal_load(q);
-    else return *q;
-}
-template <bool NT>
-__device__ __forceinline__ void st_stream_f(float* p, v4f v) {
-    v4f* q = reinterpret_cast<v4f*>(p);
-    if constexpr (NT) __builtin_nontemporal_store(v, q);
+    if constexpr (kNtCopy) asm volatile("global_store_dwordx4 %0, %1, off nt sc1\n\ts_nop 1" ::"v"(q), "v"(v) : "memory");
     else *q = v;
 }
 
@@ -1014,9 +1005,52 @@ __device__ __forceinline__ void adam_scalar(int64_t e, float* w, float* m, float
     s[e] = static_cast<uint16_t>(narrow<D>(ww));
 }
 
-// Elements [b, b + n) of the flat arrays, one piece, sub-block `sub`.
-// `skip` (the non-finite flag) is tested only after the vector loads are
-// issued, so its load never delays them; a skipped step writes nothing.
+// One wave's 256*Q consecutive elements [wb, wb + 256*Q): lane l holds
+// elements wb + 256k + 4l .. + 3 for k < Q, so every load and store
+// instruction of the wave covers one contiguous run (1 KB of an fp32
+// array, 512 B of a 16-bit one) and writes whole cache lines.  Loads and
+// stores are non-temporal: each byte is touched once per step.  `skip`
+// (the non-finite flag) is tested after the loads are issued.
+template <int D, int Q>
+__device__ __forceinline__ void adam_quads(int64_t wb, int lane, float* __restrict__ w, float* __restrict__ m,
+                                           float* __restrict__ v, const uint16_t* __restrict__ g,
+                                           uint16_t* __restrict__ s, float scale, bool skip, const AdamConsts& c) {
+    v4f W[Q], M[Q], V[Q];
+    v2u G[Q];
+#pragma unroll
+    for (int k = 0; k < Q; ++k) {
+        const int64_t e = wb + 256 * k + 4 * lane;
+        W[k] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(w + e));
+        M[k] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(m + e));
+        V[k] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(v + e));
+        G[k] = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(g + e));
+    }
+    if (skip) return;
+#pragma unroll
+    for (int k = 0; k < Q; ++k) {
+        const int64_t e = wb + 256 * k + 4 * lane;
+        float ww[4], mm[4], vv[4];
+        uint32_t out[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            ww[q] = W[k][q];
+            mm[q] = M[k][q];
+            vv[q] = V[k][q];
+            const uint32_t gw = G[k][q >> 1];
+            adam1(ww[q], mm[q], vv[q], widen<D>((q & 1) ? hi16(gw) : lo16(gw)), scale, c);
+            out[q] = narrow<D>(ww[q]);
+        }
+        __builtin_nontemporal_store(v4f{ww[0], ww[1], ww[2], ww[3]}, reinterpret_cast<v4f*>(w + e));
+        __builtin_nontemporal_store(v4f{mm[0], mm[1], mm[2], mm[3]}, reinterpret_cast<v4f*>(m + e));
+        __builtin_nontemporal_store(v4f{vv[0], vv[1], vv[2], vv[3]}, reinterpret_cast<v4f*>(v + e));
+        __builtin_nontemporal_store(v2u{pack2(out[0], out[1]), pack2(out[2], out[3])}, reinterpret_cast<v2u*>(s + e));
+    }
+}
+
+// Elements [b, b + n) of the flat arrays, one piece, sub-block `sub`: the
+// head elements (until index % 8 == 0, where every array is 16-byte aligned
+// when its base is), whole waves of 512*kAdamGPT elements as quads, and a
+// wave block that runs past the end, element by element, as the tail.
 template <int D, bool VEC>
 __device__ __forceinline__ void adam_piece(int64_t b, int64_t n, int sub, int t, float* __restrict__ w,
                                            float* __restrict__ m, float* __restrict__ v,
@@ -1028,60 +1062,22 @@ __device__ __forceinline__ void adam_piece(int64_t b, int64_t n, int sub, int t,
             adam_scalar<D>(b + i, w, m, v, g, s, scale, c);
         return;
     } else {
-        int64_t h = (8 - (b & 7)) & 7;     // with 16-byte aligned bases, index % 8 == 0 is aligned for all
+        int64_t h = (8 - (b & 7)) & 7;
         if (h > n) h = n;
         b += h;
         n -= h;
-        const int64_t ng = n >> 3;
-        const int64_t i0 = int64_t(sub) * kBlock * kAdamGPT;
-        v4f W[kAdamGPT][2], M[kAdamGPT][2], V[kAdamGPT][2];
-        v4u G[kAdamGPT];
-#pragma unroll
-        for (int u = 0; u < kAdamGPT; ++u) {
-            const int64_t i = i0 + t + int64_t(u) * kBlock;
-            if (i < ng) {
-                const int64_t e = b + 8 * i;
-                W[u][0] = ld_stream_f<kNtAdamLd>(w + e);
-                W[u][1] = ld_stream_f<kNtAdamLd>(w + e + 4);
-                M[u][0] = ld_stream_f<kNtAdamLd>(m + e);
-                M[u][1] = ld_stream_f<kNtAdamLd>(m + e + 4);
-                V[u][0] = ld_stream_f<kNtAdamLd>(v + e);
-                V[u][1] = ld_stream_f<kNtAdamLd>(v + e + 4);
-                G[u] = ld_stream<kNtAdamLd>(g + e);
+        const int64_t ng = n >> 3;                                          // groups of 8
+        const int64_t wg0 = int64_t(sub) * kBlock * kAdamGPT + int64_t(t >> 6) * 64 * kAdamGPT;   // wave's first
+        if (wg0 + 64 * kAdamGPT <= ng) {
+            adam_quads<D, 2 * kAdamGPT>(b + 8 * wg0, t & 63, w, m, v, g, s, scale, skip, c);
+        } else if (!skip && wg0 < ng) {
+            for (int e = 0; e < 8 * kAdamGPT; ++e) {
+                const int64_t k = e * 64 + (t & 63);                         // element within the wave block
+                if (wg0 + (k >> 3) < ng) adam_scalar<D>(b + 8 * wg0 + k, w, m, v, g, s, scale, c);
             }
         }
         if (skip) return;
         if (sub == 0 && t < h) adam_scalar<D>(b - h + t, w, m, v, g, s, scale, c);
-#pragma unroll
-        for (int u = 0; u < kAdamGPT; ++u) {
-            const int64_t i = i0 + t + int64_t(u) * kBlock;
-            if (i < ng) {
-                const int64_t e = b + 8 * i;
-                float ww[8], mm[8], vv[8];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    ww[q] = W[u][0][q]; ww[q + 4] = W[u][1][q];
-                    mm[q] = M[u][0][q]; mm[q + 4] = M[u][1][q];
-                    vv[q] = V[u][0][q]; vv[q + 4] = V[u][1][q];
-                }
-                uint32_t out[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const uint32_t gw = G[u][q >> 1];
-                    const float gf = widen<D>((q & 1) ? hi16(gw) : lo16(gw));
-                    adam1(ww[q], mm[q], vv[q], gf, scale, c);
-                    out[q] = narrow<D>(ww[q]);
-                }
-                st_stream_f<kNtAdamSt>(w + e, v4f{ww[0], ww[1], ww[2], ww[3]});
-                st_stream_f<kNtAdamSt>(w + e + 4, v4f{ww[4], ww[5], ww[6], ww[7]});
-                st_stream_f<kNtAdamSt>(m + e, v4f{mm[0], mm[1], mm[2], mm[3]});
-                st_stream_f<kNtAdamSt>(m + e + 4, v4f{mm[4], mm[5], mm[6], mm[7]});
-                st_stream_f<kNtAdamSt>(v + e, v4f{vv[0], vv[1], vv[2], vv[3]});
-                st_stream_f<kNtAdamSt>(v + e + 4, v4f{vv[4], vv[5], vv[6], vv[7]});
-                st_stream<kNtAdamSt>(s + e, v4u{pack2(out[0], out[1]), pack2(out[2], out[3]),
-                                              pack2(out[4], out[5]), pack2(out[6], out[7])});
-            }
-        }
         const int64_t rem = n & 7;
         if (sub == kAdamSub - 1 && t < rem) adam_scalar<D>(b + ng * 8 + t, w, m, v, g, s, scale, c);
     }
@@ -1144,20 +1140,33 @@ __global__ __launch_bounds__(kBlock) void k_init_master(const Span* __restrict__
 
 inline dim3 grid_of(int64_t n) { return dim3(static_cast<uint32_t>(n)); }
 
+// Dynamic LDS the vector Adam kernels reserve (and never use): with 160 KB
+// of LDS per CU it lets two of their workgroups (eight waves) be resident
+// per CU.  Adam streams eight arrays at once; at full residency their
+// concurrent access streams slow HBM down (measured in one process on the
+// same buffers: 4.74 ms at two workgroups per CU, 5.06 at three, 5.29 at
+// eight, bit-identical results).
+constexpr unsigned kAdamLdsReserve = 56 * 1024;
+
 // Timing hook: when a host thread has set events, its next launch records
 // the kernel's own start and end timestamps into them (hipExtLaunchKernel).
 thread_local hipEvent_t t_start = nullptr;
 thread_local hipEvent_t t_stop = nullptr;
 
 template <typename K, typename... A>
-void launch(K kernel, dim3 grid, dim3 block, hipStream_t stream, A... args) {
+void launch_shm(K kernel, dim3 grid, dim3 block, unsigned shm, hipStream_t stream, A... args) {
     if (t_start != nullptr || t_stop != nullptr) {
         hipEvent_t a = t_start, b = t_stop;
         t_start = t_stop = nullptr;
-        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, a, b, 0, args...);
+        hipExtLaunchKernelGGL(kernel, grid, block, shm, stream, a, b, 0, args...);
     } else {
-        hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+        hipLaunchKernelGGL(kernel, grid, block, shm, stream, args...);
     }
+}
+
+template <typename K, typename... A>
+void launch(K kernel, dim3 grid, dim3 block, hipStream_t stream, A... args) {
+    launch_shm(kernel, grid, block, 0, stream, args...);
 }
 
 }  // namespace
@@ -1389,10 +1398,10 @@ hipError_t launch_adam(int32_t dtype, const Span* spans, int64_t n_spans, float*
     if (n_spans <= 0) return hipSuccess;
     const dim3 g = grid_of(n_spans * kAdamSub), b(kBlock);
     if (dtype == kFP16) {
-        if (vec_ok) launch((k_adam<kFP16, true>), g, b, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
+        if (vec_ok) launch_shm((k_adam<kFP16, true>), g, b, kAdamLdsReserve, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
         else launch((k_adam<kFP16, false>), g, b, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
     } else {
-        if (vec_ok) launch((k_adam<kBF16, true>), g, b, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
+        if (vec_ok) launch_shm((k_adam<kBF16, true>), g, b, kAdamLdsReserve, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
         else launch((k_adam<kBF16, false>), g, b, stream, spans, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
     }
     return hipGetLastError();
@@ -1405,10 +1414,10 @@ hipError_t launch_adam_inline(int32_t dtype, const AdamInline& plan, float* mast
     if (n_pieces <= 0) return hipSuccess;
     const dim3 g = grid_of(n_pieces * kAdamSub), b(kBlock);
     if (dtype == kFP16) {
-        if (vec_ok) launch((k_adam_inline<kFP16, true>), g, b, stream, plan, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
+        if (vec_ok) launch_shm((k_adam_inline<kFP16, true>), g, b, kAdamLdsReserve, stream, plan, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
         else launch((k_adam_inline<kFP16, false>), g, b, stream, plan, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
     } else {
-        if (vec_ok) launch((k_adam_inline<kBF16, true>), g, b, stream, plan, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
+        if (vec_ok) launch_shm((k_adam_inline<kBF16, true>), g, b, kAdamLdsReserve, stream, plan, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
         else launch((k_adam_inline<kBF16, false>), g, b, stream, plan, master, exp_avg, exp_avg_sq, grad, shard, scale, nonfinite, c);
     }
     return hipGetLastError();

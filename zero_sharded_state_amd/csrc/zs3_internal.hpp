@@ -44,7 +44,8 @@ constexpr int kBlock = 256;             // threads per workgroup (4 wave64)
 #define ZS3_ADAM_SUB 8
 #endif
 // Non-temporal hints per family: on MI355X they help the copies, the
-// reduce-scatter and the norm, and slow the Adam pass (measured).
+// reduce-scatter and the norm (Adam's vector path always uses them, with
+// whole-line accesses and capped residency; see kernels.hip).
 #ifndef ZS3_NT_COPY
 #define ZS3_NT_COPY 1
 #endif
@@ -53,9 +54,6 @@ constexpr int kBlock = 256;             // threads per workgroup (4 wave64)
 #endif
 #ifndef ZS3_NT_NORM
 #define ZS3_NT_NORM 1
-#endif
-#ifndef ZS3_NT_ADAM
-#define ZS3_NT_ADAM 0
 #endif
 
 constexpr int kCopyVPT = ZS3_COPY_VPT;
@@ -75,8 +73,6 @@ constexpr int64_t kAdamPiece = int64_t(kBlock) * kAdamGPT * 8 * kAdamSub;
 constexpr bool kNtCopy = ZS3_NT_COPY != 0;
 constexpr bool kNtRs = ZS3_NT_RS != 0;
 constexpr bool kNtNorm = ZS3_NT_NORM != 0;
-constexpr bool kNtAdamLd = ZS3_NT_ADAM == 1 || ZS3_NT_ADAM == 2;   // 1: loads and stores, 2: loads only
-constexpr bool kNtAdamSt = ZS3_NT_ADAM == 1 || ZS3_NT_ADAM == 3;   // 3: stores only
 
 // A contiguous copy: dst[0 .. count) = src[0 .. count), or zeros if src is
 // null; if dst2 is set, also dst2[0 .. count2) = src[0 .. count2) from the
