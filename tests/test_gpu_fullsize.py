@@ -339,3 +339,77 @@ def test_fullsize_calls_on_sampled_parameters(name, rank):
     finally:
         step.destroy()
         del step
+
+
+# --------------------------------------------------------------------------
+# c4 rank 0: every element of one whole step
+# --------------------------------------------------------------------------
+
+@pytest.mark.timeout(900)
+def test_c4_rank0_whole_step_every_element():
+    """One whole c4 step of rank 0 in bench.py's default launch configuration
+    (gather buckets over two streams, gradient buckets over three, received
+    slices per bucket, fused norm), then every element of the rank's flat
+    gradient, fp32 master, momentum, variance and 16-bit shard compared with
+    the oracle, parameter by parameter (rank 0's own range of every parameter
+    starts at element 0, so a one-parameter layout and the received slices
+    are all the oracle needs; host memory stays bounded by the largest
+    parameter).  Bit-exact, with Adam run on the scale the GPU used; that
+    scale within 1 ulp of the oracle's and the norm within 1e-5."""
+    import torch
+
+    import bench
+    cfg = get_config("c4")
+    N, dt, rank = cfg.world_size, cfg.dtype, 0
+    note("c4 rank 0 whole step: set-up")
+    step = bench.make_step(cfg, rank, rs_streams=3, gather_streams=2, fuse_norm=True, recv_layout="bucket")
+    try:
+        bench.fill_inputs(step, cfg)
+        sync()
+        shard0 = h16(step.shard).copy()                       # the shard before the step (2 GB)
+        note("c4 rank 0 whole step: one step")
+        step.step()
+        sync()
+        o = step.outs.cpu().numpy()
+        gpu_norm = float(o[0])
+        gpu_scale = np.float32(o[1:2].view(np.float32)[0])
+        assert int(o[1:2].view(np.int32)[1]) == 0
+        sumsq = step.sumsq.cpu().numpy()
+        # pass 1: the flat gradient, and the oracle's partial sums
+        part = pers = 0.0
+        for p in step.params:
+            d, n, ps, off = p["ds_id"], p["numel"], p["partition_size"], p["shard_offset"]
+            lo, hi = p["own"]
+            assert lo == 0
+            L1 = oracle.make_layout(N, cfg.threshold, [d], [n])
+            grads = [{d: h16(step.recv[step.recv_index(v, d):step.recv_index(v, d) + hi])} for v in range(N)]
+            ref = np.zeros(ps, np.uint16)
+            oracle.reduce_scatter(L1, rank, dt, [d], grads, ref)
+            got = h16(step.grad[off:off + ps])
+            assert np.array_equal(got, ref), f"flat gradient of ds_id {d}"
+            a, q = oracle.grad_norm_partial(L1, rank, dt, ref)
+            part += a
+            pers += q
+        peers = [float(sumsq[v]) if v != rank else part for v in range(N)]
+        norm, coef, scale, bad = oracle.grad_norm_finalize(peers, pers, cfg.max_norm)
+        assert not bad
+        assert abs(gpu_norm - norm) <= 1e-5 * norm
+        assert abs(float(gpu_scale) - float(scale)) <= float(np.spacing(np.float32(scale)))
+        assert float(sumsq[rank]) == pytest.approx(part, rel=1e-12)
+        # pass 2: Adam (t = 1) on every parameter's range, with the GPU's scale
+        hp = _hp(cfg, 1)
+        for p in step.params:
+            d, n, ps, off = p["ds_id"], p["numel"], p["partition_size"], p["shard_offset"]
+            L1 = oracle.make_layout(N, cfg.threshold, [d], [n])
+            g = h16(step.grad[off:off + ps])
+            sh = shard0[off:off + ps].copy()
+            w, m, v_ = oracle.init_state(sh, dt)
+            oracle.adam_step(L1, rank, dt, 0, ps, w, m, v_, g, sh, gpu_scale, False, hp)
+            for name, t, ref in (("master", step.master, w), ("exp_avg", step.exp_avg, m),
+                                 ("exp_avg_sq", step.exp_avg_sq, v_)):
+                got = t[off:off + ps].cpu().numpy()
+                assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"{name} of ds_id {d}"
+            assert np.array_equal(h16(step.shard[off:off + ps]), sh), f"16-bit shard of ds_id {d}"
+        note(f"c4 rank 0 whole step: every element equal (norm {gpu_norm:.6g})")
+    finally:
+        step.destroy()
