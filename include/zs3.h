@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define ZS3_ABI_VERSION 2
+#define ZS3_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define ZS3_API __attribute__((visibility("default")))

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol(L):
     assert sorted(zs.EXPORTS) == syms
     for s in syms:
         assert hasattr(L, s), s
-    assert zs.zs3_abi_version() == 2
+    assert zs.zs3_abi_version() == 3
     assert zs.zs3_status_str(-5).startswith("persistent")
 
 

@@ -78,15 +78,15 @@ struct Key {
     bool operator==(const Key& o) const { return w == o.w; }
 };
 
+// One multiply-xorshift round per 64-bit word (a call's key can hold tens of
+// thousands of words: every pointer of a single-launch reduce-scatter).
 struct KeyHash {
     size_t operator()(const Key& k) const {
-        uint64_t h = 1469598103934665603ull;
+        uint64_t h = 0x9e3779b97f4a7c15ull ^ k.w.size();
         for (int64_t x : k.w) {
-            uint64_t v = static_cast<uint64_t>(x);
-            for (int i = 0; i < 8; ++i) {
-                h ^= (v >> (8 * i)) & 0xff;
-                h *= 1099511628211ull;
-            }
+            h ^= static_cast<uint64_t>(x) + 0x9e3779b97f4a7c15ull + (h << 6) + (h >> 2);
+            h *= 0xff51afd7ed558ccdull;
+            h ^= h >> 32;
         }
         return static_cast<size_t>(h);
     }
@@ -1048,21 +1048,35 @@ zs3_status zs3_reduce_scatter_local(zs3_layout_t L, int32_t rank, int32_t dtype,
     if ((s = check_partials(L, partials, grad_flat)) != ZS3_OK) return s;
     const int32_t N = L->world;
     uint16_t* gbase = static_cast<uint16_t*>(grad_flat);
+    // no source may overlap a written range (the parameters' partitions of
+    // grad_flat, and partials): one sort-and-sweep over every range
+    std::vector<Range> ranges;
+    ranges.reserve(static_cast<size_t>(n) * (N + 1) + 1);
     for (int32_t i = 0; i < n; ++i) {
         const Slot& p = L->params[pos[i]];
+        const uintptr_t w = reinterpret_cast<uintptr_t>(gbase + p.offset);
+        ranges.push_back(Range{w, w + 2 * static_cast<uintptr_t>(p.ps), true, -1});
         const int64_t real = p.real(rank);
+        if (real == 0) continue;
         for (int32_t v = 0; v < N; ++v) {
             const void* q = src[static_cast<int64_t>(i) * N + v];
-            if (real == 0) continue;
             if ((s = check_ptr16(q, "src[i*N+v]")) != ZS3_OK) return s;
-            for (int32_t j = 0; j < n; ++j) {
-                const Slot& o = L->params[pos[j]];
-                if (overlap(q, 2 * real, gbase + o.offset, 2 * o.ps))
-                    return fail(ZS3_EALIAS, "src[%d*N+%d] overlaps the written part of grad_flat", i, v);
-            }
-            if (partials != nullptr && overlap(q, 2 * real, partials, 8 * L->n_slots))
-                return fail(ZS3_EALIAS, "src[%d*N+%d] overlaps partials", i, v);
+            const uintptr_t x = reinterpret_cast<uintptr_t>(q);
+            ranges.push_back(Range{x, x + 2 * static_cast<uintptr_t>(real), false, i * N + v});
         }
+    }
+    if (partials != nullptr) {
+        const uintptr_t x = reinterpret_cast<uintptr_t>(partials);
+        ranges.push_back(Range{x, x + 8 * static_cast<uintptr_t>(L->n_slots), true, -2});
+    }
+    const Range* other = nullptr;
+    if (const Range* bad = first_overlap(&ranges, &other)) {
+        const Range* rd = bad->write ? other : bad;
+        const Range* wr = bad->write ? bad : other;
+        if (rd->write)
+            return fail(ZS3_EALIAS, "partials overlaps grad_flat");
+        return fail(ZS3_EALIAS, "src[%d*N+%d] overlaps %s", rd->tag / N, rd->tag % N,
+                    wr->tag == -2 ? "partials" : "the written part of grad_flat");
     }
     Key key{{kOpReduce, device_id(), rank, reinterpret_cast<int64_t>(grad_flat)}};
     for (int32_t k : order) {
