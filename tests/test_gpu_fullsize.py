@@ -14,6 +14,9 @@ over three streams).
   inputs, its outputs checked on a sample of whole parameters (the oracle
   recomputes those parameters only) or, for the norm, over the whole flat
   gradient the reduce-scatter produced.
+* One whole step of c4 rank 0 and of c5 rank 63 in bench.py's default launch
+  configuration: every element of the flat gradient, master, momentum,
+  variance and shard against the oracle.
 """
 
 import gc
@@ -411,5 +414,86 @@ def test_c4_rank0_whole_step_every_element():
                 assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"{name} of ds_id {d}"
             assert np.array_equal(h16(step.shard[off:off + ps]), sh), f"16-bit shard of ds_id {d}"
         note(f"c4 rank 0 whole step: every element equal (norm {gpu_norm:.6g})")
+    finally:
+        step.destroy()
+
+
+# --------------------------------------------------------------------------
+# c5 rank 63: every element of one whole step (N = 64, fp16, ragged)
+# --------------------------------------------------------------------------
+
+@pytest.mark.timeout(900)
+def test_c5_rank63_whole_step_every_element():
+    """One whole c5 step of the last rank (N = 64, fp16, every partitioned
+    tensor padded; the wide reduce-scatter) in bench.py's default launch
+    configuration, then every element of the rank's flat gradient, fp32
+    master, momentum, variance and 16-bit shard compared with the oracle,
+    parameter by parameter.  The last rank's own range starts at 63 x
+    partition_size, so the oracle's owner-side reduce takes the 64 received
+    slices themselves (its reading of the arithmetic is the reduce-scatter's,
+    R23); persistent parameters, whole on every rank, go through the oracle's
+    reduce-scatter.  Host memory stays bounded by 64 slices of the largest
+    parameter.  Bit-exact, with Adam run on the scale the GPU used; that
+    scale within 1 ulp of the oracle's and the norm within 1e-5."""
+    import bench
+    cfg = get_config("c5")
+    N, dt = cfg.world_size, cfg.dtype
+    rank = N - 1
+    note(f"c5 rank {rank} whole step: set-up")
+    step = bench.make_step(cfg, rank, rs_streams=3, gather_streams=2, fuse_norm=True, recv_layout="bucket")
+    try:
+        bench.fill_inputs(step, cfg)
+        sync()
+        shard0 = h16(step.shard).copy()
+        note(f"c5 rank {rank} whole step: one step")
+        step.step()
+        sync()
+        o = step.outs.cpu().numpy()
+        gpu_norm = float(o[0])
+        gpu_scale = np.float32(o[1:2].view(np.float32)[0])
+        assert int(o[1:2].view(np.int32)[1]) == 0
+        sumsq = step.sumsq.cpu().numpy()
+        part = pers = 0.0
+        n_padded = 0
+        for p in step.params:
+            d, n, ps, off = p["ds_id"], p["numel"], p["partition_size"], p["shard_offset"]
+            lo, hi = p["own"]
+            real = hi - lo
+            L1 = oracle.make_layout(N, cfg.threshold, [d], [n])
+            ref = np.full(ps, 0xFFFF, np.uint16)
+            slices = [h16(step.recv[step.recv_index(v, d):step.recv_index(v, d) + real]) for v in range(N)]
+            if p["persistent"]:
+                assert lo == 0 and real == n
+                oracle.reduce_scatter(L1, rank, dt, [d], [{d: s} for s in slices], ref)
+            else:
+                n_padded += int(real < ps)
+                received = [np.concatenate([s, np.zeros(ps - real, np.uint16)]) for s in slices]
+                oracle.scatter_reduce(L1, rank, dt, [d], received, ref)
+            got = h16(step.grad[off:off + ps])
+            assert np.array_equal(got, ref), f"flat gradient of ds_id {d}"
+            a, q = oracle.grad_norm_partial(L1, rank, dt, ref)
+            part += a
+            pers += q
+        assert n_padded > 100, "the last rank must hold padding in most partitioned tensors"
+        peers = [float(sumsq[v]) if v != rank else part for v in range(N)]
+        norm, coef, scale, bad = oracle.grad_norm_finalize(peers, pers, cfg.max_norm)
+        assert not bad
+        assert abs(gpu_norm - norm) <= 1e-5 * norm
+        assert abs(float(gpu_scale) - float(scale)) <= float(np.spacing(np.float32(scale)))
+        assert float(sumsq[rank]) == pytest.approx(part, rel=1e-12)
+        hp = _hp(cfg, 1)
+        for p in step.params:
+            d, n, ps, off = p["ds_id"], p["numel"], p["partition_size"], p["shard_offset"]
+            L1 = oracle.make_layout(N, cfg.threshold, [d], [n])
+            g = h16(step.grad[off:off + ps])
+            sh = shard0[off:off + ps].copy()
+            w, m, v_ = oracle.init_state(sh, dt)
+            oracle.adam_step(L1, rank, dt, 0, ps, w, m, v_, g, sh, gpu_scale, False, hp)
+            for name, t, want in (("master", step.master, w), ("exp_avg", step.exp_avg, m),
+                                  ("exp_avg_sq", step.exp_avg_sq, v_)):
+                got = t[off:off + ps].cpu().numpy()
+                assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"{name} of ds_id {d}"
+            assert np.array_equal(h16(step.shard[off:off + ps]), sh), f"16-bit shard of ds_id {d}"
+        note(f"c5 rank {rank} whole step: every element equal (norm {gpu_norm:.6g})")
     finally:
         step.destroy()
