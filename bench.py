@@ -269,21 +269,30 @@ def cpu_baseline(step, cfg, layers: int):
     grad_flat = np.zeros(L.shard_numel, np.uint16)
     hp = oracle.AdamHParams(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, 1)
 
-    t0 = time.perf_counter()
+    t = [time.perf_counter()]
     for _ in range(2):                                       # forward + backward all-gather
         for b in buckets:
             oracle.pack(L, r, b, shard)
             oracle.unpack(L, b, chunks[tuple(b)])
+    t.append(time.perf_counter())
     oracle.reduce_scatter(L, r, dt, ids[::-1], grads, grad_flat)
+    t.append(time.perf_counter())
     a, q = oracle.grad_norm_partial(L, r, dt, grad_flat)
     norm, coef, scale, bad = oracle.grad_norm_finalize([a] * N, q, cfg.max_norm)
+    t.append(time.perf_counter())
     oracle.adam_step(L, r, dt, 0, L.shard_numel, master, m, v_, grad_flat, shard, scale, bad, hp)
-    secs = time.perf_counter() - t0
+    t.append(time.perf_counter())
+    secs = t[-1] - t[0]
 
     part_real = sum(L.own_range(p, r)[1] - L.own_range(p, r)[0] for p in L.params if not p.persistent)
     own = sum(L.own_range(p, r)[1] - L.own_range(p, r)[0] for p in L.params)
     F = sum(sum(L.slot(d).numel for d in b) for b in buckets)
-    nbytes = 2 * 4 * part_real + 2 * 4 * F + (2 * N * own + 2 * own) + 2 * own + 28 * own
+    phase_bytes = {"gather": 2 * 4 * part_real + 2 * 4 * F, "reduce_scatter": 2 * N * own + 2 * own,
+                   "grad_norm": 2 * own, "adam": 28 * own}
+    nbytes = sum(phase_bytes.values())
+    kernels = {}
+    for (name, b), t0, t1 in zip(phase_bytes.items(), t, t[1:]):
+        kernels[name] = {"s": round(t1 - t0, 4), "GBps": round(b / (t1 - t0) / 1e9, 4) if t1 > t0 else None}
     return {
         "value": round(nbytes / secs / 1e9, 4),
         "unit": "GB/s",
@@ -294,6 +303,7 @@ def cpu_baseline(step, cfg, layers: int):
                    f"{nbytes / 1e9:.3f} GB algorithmic in {secs:.2f} s"),
         "params_per_s": round(own / secs, 1),
         "host_cores_available": len(os.sched_getaffinity(0)),
+        "kernels": kernels,
     }
 
 
