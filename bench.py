@@ -469,7 +469,8 @@ def main():
         kernels[name] = {"ms": round(ms, 4), "bytes": phase_bytes[name],
                          "GBps": round(phase_bytes[name] / (ms * 1e-3) / 1e9, 1) if phase_bytes[name] else None,
                          "hbm_frac": (round(phase_bytes[name] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
-                                      if phase_bytes[name] else None)}
+                                      if phase_bytes[name] else None),
+                         "params_per_s": round(step.own_real / (ms * 1e-3), 1) if ms > 0 else None}
 
     # Roofline entry of the dominant kernel: the fused gather (pack + unpack
     # of one bucket, k_copy<4>), bytes per launch over the average launch
