@@ -1,6 +1,7 @@
-"""bench.py's command-line contract that needs no GPU: asking for more than
-one GPU ends at once with a message on one JSON line; the bucket-size
-overrides (CPU only)."""
+"""bench.py's contract parts that need no GPU: asking for more than one GPU
+ends at once with a message on one JSON line; the bucket-size overrides;
+the code digest that ties the committed counter summary to the kernel
+sources, and the traffic entry it gates."""
 
 import json
 import os
@@ -35,3 +36,33 @@ def test_bucket_size_overrides_make_one_bucket_per_phase():
     assert len(oracle.gather_buckets(L, cfg.prefetch_bucket_size)) == 3
     only_reduce = bench.with_bucket_sizes(cfg, None, 7)
     assert only_reduce.prefetch_bucket_size == cfg.prefetch_bucket_size and only_reduce.reduce_bucket_size == 7
+
+
+def test_code_digest_ignores_comments_and_layout_only():
+    """The digest that ties profiles/ to the kernel sources changes with the
+    code and not with comments or whitespace."""
+    sys.path.insert(0, ROOT)
+    import bench
+    code = "int f(int x) {\n  return x + 1; // one\n}\n/* block\n comment */\n"
+    same = "int f(int x) { return x + 1; }   // other words\n"
+    other = "int f(int x) { return x + 2; }\n"
+    assert bench._code_only(code) == bench._code_only(same)
+    assert bench._code_only(code) != bench._code_only(other)
+
+
+def test_committed_traffic_summary_matches_the_current_kernels(monkeypatch):
+    """profiles/gather_traffic_c4.json was taken on the current kernel
+    sources, so the bench line carries its HBM bytes per launch; with any
+    other digest the entry is withheld (None)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    with open(os.path.join(ROOT, "profiles", "gather_traffic_c4.json")) as fh:
+        t = json.load(fh)
+    assert t["source_digest"] == bench.source_digest()
+    hbm = bench.traffic_entry("c4")
+    assert abs(hbm - (t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"])) <= 1    # each rounded down
+    # fetched plus written bytes sit just below the algorithmic count: the own part is read once
+    assert 0.9 * t["algorithmic_bytes_per_launch"] < hbm <= t["algorithmic_bytes_per_launch"]
+    monkeypatch.setattr(bench, "source_digest", lambda: "0" * 16)
+    assert bench.traffic_entry("c4") is None
+    assert bench.traffic_entry("no_such_workload") is None
