@@ -46,9 +46,9 @@ def test_c_caller_of_the_device_entry_points(tmp_path):
     cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"),
            os.path.join(HERE, "c_abi_device.c"), "-L", PKG, "-lzs3", f"-Wl,-rpath,{PKG}",
-           "-L", os.path.join(rocm, "lib"), "-lamdhip64", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-o", exe]
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-lm", "-o", exe]
     b = subprocess.run(cmd, capture_output=True, text=True)
     assert b.returncode == 0, b.stdout + b.stderr
-    note("c_abi_device: partition, gather, reduce-scatter from C")
+    note("c_abi_device: partition, gathers, reduce-scatter, norm, master, Adam from C")
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
