@@ -1,5 +1,7 @@
 // Seeded random exercise of the zs3 host entry points (layout, queries,
-// bucket and sub-group planning, the coordinator, argument errors), for
+// bucket and sub-group planning, the coordinator, argument errors, and the
+// aliasing checks of the device entry points, which reject a call before
+// any device work), for
 // AddressSanitizer / UBSan / ThreadSanitizer builds of the host code.  No
 // device calls.  Runs once on the main thread, then on four threads at once,
 // each with its own seed and its own layouts (the library keeps no shared
@@ -11,6 +13,7 @@
 #include <cstring>
 #include <string>
 #include <thread>
+#include <utility>
 #include <vector>
 
 #include "zs3.h"
@@ -128,6 +131,71 @@ void fuzz(uint64_t seed, int iters) {
                 check(zs3_coord_fetch(C, nm, &cnt, kinds, gst, buf.data()) == ZS3_EINVAL, "bad module", it);
                 zs3_coord_destroy(C);
             }
+        }
+        // aliasing: a source inside a written range, or two outputs that
+        // touch, is rejected before any device work (the sort-and-sweep
+        // over every byte range of the call; the addresses are never used)
+        if (n > 0) {
+            const uintptr_t base = uintptr_t(1) << 40;
+            const int32_t r = static_cast<int32_t>(uniform(0, N - 1));
+            std::vector<const void*> src(static_cast<size_t>(n) * N);
+            std::vector<std::pair<int64_t, int64_t>> written;
+            int64_t victim = -1;
+            for (int32_t i = 0; i < n; ++i) {
+                int64_t nm = 0, ps = 0, off = 0, lo = 0, hi = 0;
+                int32_t pers = 0;
+                check(zs3_layout_param(L, ids[i], &nm, &ps, &pers, &off) == ZS3_OK, "param", it);
+                check(zs3_layout_own_range(L, ids[i], r, &lo, &hi) == ZS3_OK, "own range", it);
+                if (hi > lo && victim < 0) victim = i;
+                written.emplace_back(off, ps);
+                for (int32_t v = 0; v < N; ++v)
+                    src[static_cast<size_t>(i) * N + v] =
+                        reinterpret_cast<const void*>(base + (uintptr_t(1) << 34) + 2 * uniform(0, 1 << 28));
+            }
+            if (victim >= 0) {
+                // the victim's first source starts inside some parameter's written range
+                const auto& w = written[uniform(0, n - 1)];
+                const uintptr_t grad = base;
+                src[static_cast<size_t>(victim) * N] =
+                    reinterpret_cast<const void*>(grad + 2 * (w.first + uniform(0, w.second - 1)));
+                check(zs3_reduce_scatter_local(L, r, ZS3_BF16, n, ids.data(), src.data(),
+                                               reinterpret_cast<void*>(grad), nullptr, nullptr) == ZS3_EALIAS,
+                      "reduce-scatter alias", it);
+            }
+            // two buckets whose gathered buffers overlap
+            std::vector<int64_t> part;
+            for (int32_t i = 0; i < n; ++i) {
+                int32_t pers = 0;
+                (void)zs3_layout_param(L, ids[i], nullptr, nullptr, &pers, nullptr);
+                if (!pers) part.push_back(ids[i]);
+            }
+            if (part.size() >= 2) {
+                const int32_t starts[3] = {0, 1, 2};
+                const uintptr_t shard = base, full0 = base + (uintptr_t(1) << 36);
+                void* owns[2] = {reinterpret_cast<void*>(base + (uintptr_t(1) << 35)),
+                                 reinterpret_cast<void*>(base + (uintptr_t(1) << 35) + (uintptr_t(1) << 30))};
+                void* fulls[2] = {reinterpret_cast<void*>(full0), reinterpret_cast<void*>(full0)};   // same start
+                std::vector<const void*> rch(2 * static_cast<size_t>(N));
+                for (int32_t b = 0; b < 2; ++b)
+                    for (int32_t v = 0; v < N; ++v)
+                        rch[static_cast<size_t>(b) * N + v] =
+                            v == r ? owns[b]
+                                   : reinterpret_cast<const void*>(base + (uintptr_t(1) << 37) +
+                                                                   (uintptr_t(b * N + v) << 29));
+                check(zs3_gather_coalesced_buckets(L, r, ZS3_BF16, 2, starts, part.data(),
+                                                   reinterpret_cast<const void*>(shard), owns, rch.data(), fulls,
+                                                   nullptr) == ZS3_EALIAS,
+                      "gather buckets alias", it);
+            }
+        }
+        // argument errors of the entry points that take plain ranges
+        {
+            float* fake = reinterpret_cast<float*>(uintptr_t(1) << 40);
+            check(zs3_init_master(L, 0, ZS3_BF16, 1, 0, fake, fake, nullptr, nullptr, nullptr) == ZS3_EINVAL,
+                  "init range", it);
+            check(zs3_grad_norm_partials_noalloc(L, 0, nullptr, nullptr, 0, 1.0, 1.0, nullptr, nullptr, nullptr,
+                                                 nullptr) == ZS3_EINVAL,
+                  "noalloc null", it);
         }
         // argument errors
         check(zs3_layout_param(L, -7, nullptr, nullptr, nullptr, nullptr) == ZS3_ENOTFOUND, "not found", it);
