@@ -4,8 +4,9 @@
 // any device work), for
 // AddressSanitizer / UBSan / ThreadSanitizer builds of the host code.  No
 // device calls.  Runs once on the main thread, then on four threads at once,
-// each with its own seed and its own layouts (the library keeps no shared
-// state; the last error is per thread).  Built and run by
+// each with its own seed and its own layouts (no state is shared between
+// layouts apart from the allocation-free norm's device scratch, which these
+// calls never reach; the last error is per thread).  Built and run by
 // tests/test_host_sanitizers.py; prints "ok".
 #include <atomic>
 #include <cstdint>
