@@ -15,8 +15,9 @@ outliers) and resident in HBM before timing starts.
 
 Default launch configuration: gather buckets dealt over two streams,
 gradient buckets over three streams, the slices each rank receives placed
-per gradient bucket, the norm fused into the reduce.  --single-launch
-gather|reduce|both makes a phase one launch over every bucket.
+per gradient bucket, the norm fused into the reduce, and one launch over
+every bucket for a phase whose pass moves less than 4 GB (--single-launch
+auto; none|gather|reduce|both choose by hand).
 Variants: --reduce-path coalesced (the non-contiguous gradient path),
 --schedule trace (gathers driven by the fetch/release coordinator over the
 forward+backward module order), --offload 1 (the fp32 optimizer state in
@@ -87,9 +88,10 @@ def parse():
     ap.add_argument("--recv-layout", default="bucket", choices=("rank", "bucket"),
                     help="where the slices the N ranks send this rank live: one shard-shaped copy per rank, or "
                          "per gradient bucket with its N slices next to each other")
-    ap.add_argument("--single-launch", default="none", choices=("none", "gather", "reduce", "both"),
+    ap.add_argument("--single-launch", default="auto", choices=("auto", "none", "gather", "reduce", "both"),
                     help="gather: each gather pass one launch over every bucket (each bucket keeps its own wire and "
-                         "gathered buffer); reduce: the gradient phase one launch over every bucket; both")
+                         "gathered buffer); reduce: the gradient phase one launch over every bucket; both; auto "
+                         "(default): one launch for a phase whose pass moves less than 4 GB")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -170,6 +172,35 @@ def with_bucket_sizes(cfg, prefetch=None, reduce=None):
     import dataclasses
     return dataclasses.replace(cfg, prefetch_bucket_size=int(prefetch or cfg.prefetch_bucket_size),
                                reduce_bucket_size=int(reduce or cfg.reduce_bucket_size))
+
+
+# A pass of per-bucket launches pays a fixed cost per launch (ramp-up, drain,
+# the kernel boundary); one launch over every bucket reads its work list from
+# device memory instead of its arguments, a cost in proportion to the bytes.
+# Measured crossover: passes of 0.3-1 GB run faster as one launch, passes of
+# 15-36 GB as per-bucket launches over several streams.
+SINGLE_LAUNCH_BELOW_BYTES = 4e9
+
+
+def auto_single_launch(cfg, rank, reduce_path="contiguous", schedule="static"):
+    """none / gather / reduce / both: one launch for each phase whose pass
+    moves fewer algorithmic bytes than SINGLE_LAUNCH_BELOW_BYTES."""
+    import zero_sharded_state_amd as zs
+    h = zs.zs3_layout_create(cfg.world_size, cfg.threshold, cfg.ds_ids, cfg.numels)
+    try:
+        N = cfg.world_size
+        gather = 0
+        for b in zs.zs3_plan_buckets(h, zs.ZS3_GATHER_BUCKETS, cfg.prefetch_bucket_size):
+            gather += sum(4 * (zs.zs3_layout_own_range(h, d, rank)[1] - zs.zs3_layout_own_range(h, d, rank)[0])
+                          + 4 * zs.zs3_layout_param(h, d)["numel"] for d in b)
+        own = sum(zs.zs3_layout_own_range(h, d, rank)[1] - zs.zs3_layout_own_range(h, d, rank)[0]
+                  for d in cfg.ds_ids)
+        reduce = (2 * N + 2) * own
+    finally:
+        zs.zs3_layout_destroy(h)
+    g = schedule == "static" and gather < SINGLE_LAUNCH_BELOW_BYTES
+    r = reduce_path == "contiguous" and reduce < SINGLE_LAUNCH_BELOW_BYTES
+    return {(False, False): "none", (True, False): "gather", (False, True): "reduce", (True, True): "both"}[(g, r)]
 
 
 def make_step(cfg, rank, rs_streams=1, gather_streams=1, fuse_norm=False, reduce_path="contiguous", offload=False,
@@ -387,8 +418,11 @@ def main():
     cfg = with_bucket_sizes(get_config(args.config), args.prefetch_bucket_size, args.reduce_bucket_size)
     rank = cfg.bench_rank if args.rank is None else args.rank
     log(f"config {cfg.name}: {cfg.title}, rank {rank}")
+    single = args.single_launch
+    if single == "auto":
+        single = auto_single_launch(cfg, rank, args.reduce_path, args.schedule)
     step = make_step(cfg, rank, args.rs_streams, args.gather_streams, bool(args.fuse_norm), args.reduce_path,
-                     bool(args.offload), args.offload_chunk, args.recv_layout, args.single_launch)
+                     bool(args.offload), args.offload_chunk, args.recv_layout, single)
     log(f"layout: S+P={step.S:,} own real={step.own_real:,} F={step.F:,} gather buckets={len(step.gather_buckets)} "
         f"reduce buckets={len(step.reduce_buckets)} sub-groups={len(step.sub_groups)}")
     t0 = time.time()
@@ -604,6 +638,7 @@ def main():
             "schedule": args.schedule, "offload": step.offload,
             "gather_streams": step.gather_streams, "recv_layout": step.recv_layout,
             "single_launch": step.single_launch,
+            "single_launch_flag": args.single_launch,
         },
         "kernels": kernels,
         "roofline": roofline,

@@ -66,3 +66,18 @@ def test_committed_traffic_summary_matches_the_current_kernels(monkeypatch):
     monkeypatch.setattr(bench, "source_digest", lambda: "0" * 16)
     assert bench.traffic_entry("c4") is None
     assert bench.traffic_entry("no_such_workload") is None
+
+
+def test_auto_launch_granularity():
+    """--single-launch auto: one launch for a phase whose pass moves less
+    than 4 GB (the small workloads), per-bucket launches for the large ones;
+    never a single gather launch under the coordinator's schedule, nor a
+    single reduce launch on the non-contiguous gradient path."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from synth import get_config
+    pick = {c: bench.auto_single_launch(get_config(c), get_config(c).bench_rank) for c in ("c1", "c2", "c3", "c4", "c5")}
+    assert pick == {"c1": "both", "c2": "both", "c3": "both", "c4": "none", "c5": "none"}
+    c2 = get_config("c2")
+    assert bench.auto_single_launch(c2, 0, reduce_path="coalesced") == "gather"
+    assert bench.auto_single_launch(c2, 0, schedule="trace") == "reduce"
