@@ -462,8 +462,8 @@ def main():
     # With --kernel-timer and several gather streams every gather launch of
     # the timed steps records its own start/end (a few us per launch).
     per_pass = 1 if step.single_gather else len(step.gather_buckets)
-    overlapped = step.gather_streams > 1 and not step.single_gather and trace is None
-    per_launch = overlapped and args.kernel_timer
+    overlapped = step.gather_streams > 1 and not step.single_gather
+    per_launch = overlapped and args.kernel_timer and trace is None
     timer = KernelTimer(2 * per_pass * args.steps if per_launch else 0)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -518,19 +518,24 @@ def main():
     gather_bytes = nbytes["gather_trace"] if trace is not None else nbytes["pack"] + nbytes["unpack"]
     gather_phase_ms = sum(phases.get(k, 0.0) for k in ("gather_fwd", "gather_bwd", "gather_trace"))
     if overlapped:
-        cal_passes = 2 * min(args.steps, 5)
-        step.gather_pass(streams=1)
+        # forward + backward passes of the static buckets, or whole steps of
+        # the coordinator's gathers, on the launch stream alone
+        cal_passes = 2 * min(args.steps, 5) if trace is None else min(args.steps, 5)
+        per_cal = per_pass if trace is None else len(trace.ops)
+        one_pass = (lambda: step.gather_pass(streams=1)) if trace is None else (lambda: trace.run(streams=1))
+        one_pass()
         e0, e1 = ev(), ev()
         e0.record(stream)
         for _ in range(cal_passes):
-            step.gather_pass(streams=1)
+            one_pass()
         e1.record(stream)
         torch.cuda.synchronize()
-        launches = cal_passes * per_pass
+        launches = cal_passes * per_cal
         avg_ms = e0.elapsed_time(e1) / launches
-        per_launch_bytes = gather_bytes / 2 / per_pass
-        measured = (f"{cal_passes} gather passes on the launch stream alone, right after the timed steps "
-                    f"(the step deals its buckets over {step.gather_streams} streams)")
+        per_launch_bytes = gather_bytes / (2 * per_pass if trace is None else per_cal)
+        what = "gather passes" if trace is None else "steps of the coordinator's gathers"
+        measured = (f"{cal_passes} {what} on the launch stream alone, right after the timed steps "
+                    f"(the step deals its gathers over {step.gather_streams} streams)")
     else:
         launches = (len(trace.ops) if trace is not None else 2 * per_pass) * args.steps
         avg_ms = gather_phase_ms / launches

@@ -114,12 +114,15 @@ class TraceGatherPass:
         del tmp
 
     # --------------------------------------------------------- device side
-    def run(self, stream=None):
+    def run(self, stream=None, streams=None):
         """One step's fetches and releases, each returned gather launched as
-        it is returned.  Returns the number of gathers."""
+        it is returned.  Every gather writes a buffer of its own, so they are
+        dealt round-robin over the step's gather streams (``streams``
+        overrides the count) and joined into the launch stream at the end.
+        Returns the number of gathers."""
         s = self.step
         lib = zs.lib()
-        st = stream if stream is not None else s._stream()
+        main, aux, handles = s._fanout(stream, s.gather_streams if streams is None else streams)
         i = 0
         for m in self.order:
             for kind, g in self._fetch(m):
@@ -127,9 +130,11 @@ class TraceGatherPass:
                     raise RuntimeError("the coordinator's gathers changed from the planned step")
                 n, ids, own, chunks, fullp = self._args[i]
                 s._ok(lib.zs3_gather_coalesced(s.h, s.rank, s.dcode, zs.ZS3_PACK | zs.ZS3_UNPACK, n, ids,
-                                               s.shard.data_ptr(), own, chunks, fullp, None, st))
+                                               s.shard.data_ptr(), own, chunks, fullp, None,
+                                               handles[i % len(handles)]))
                 i += 1
             self._release(m)
+        s._join(main, aux)
         zs.zs3_coord_release_all(self.coord)
         zs.zs3_coord_reset_step(self.coord)
         if i != len(self.ops):
