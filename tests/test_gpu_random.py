@@ -1,5 +1,5 @@
 """GPU parity on seeded random layouts: each case draws a world size (1 to
-64), a persistence threshold, up to 16 parameters with ragged sizes (mostly
+64; 128 to 1000 in a few more), a persistence threshold, up to 16 parameters with ragged sizes (mostly
 tiny, some spanning many workgroup pieces), a dtype, a rank, base-pointer
 misalignments and bucket limits, then runs the whole chain through the C
 ABI -- partition, fused gather of every gather bucket (shuffled requests),
@@ -46,8 +46,33 @@ def _case(seed):
 
 @pytest.mark.parametrize("seed", range(200))
 def test_random_layout_chain(seed):
+    _chain(seed, *_case(seed))
+
+
+def _large_world_case(seed):
+    """Many ranks (128 to 1000): every parameter split over more ranks than
+    it has elements in places (ranks holding only padding), the gathers'
+    and reduce-scatter's work lists far past what fits in kernel arguments."""
+    rng = np.random.default_rng(40_000 + seed)
+    N = int(rng.choice([128, 256, 1000]))
+    T = int(rng.choice([0, 50]))
+    n = int(rng.integers(1, 7))
+    numels = [int(rng.integers(1, 200)) if k < 0.4 else int(rng.integers(200, 6000)) for k in rng.random(n)]
+    ids = [int(x) for x in rng.choice(10 * n + 5, n, replace=False)]
+    dtype = "bf16" if rng.random() < 0.5 else "fp16"
+    r = int(rng.choice([0, N - 1, int(rng.integers(0, N))]))
+    shifts = [int(x) for x in rng.integers(0, 8, 6)]
+    return rng, N, T, ids, numels, dtype, r, shifts
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("seed", range(6))
+def test_large_world_chain(seed):
+    _chain(1000 + seed, *_large_world_case(seed))
+
+
+def _chain(seed, rng, N, T, ids, numels, dtype, r, sh):
     import torch
-    rng, N, T, ids, numels, dtype, r, sh = _case(seed)
     tag = f"random seed={seed} N={N} T={T} params={len(ids)} {dtype} rank={r}"
     h = zs.zs3_layout_create(N, T, ids, numels)
     L = oracle.make_layout(N, T, ids, numels)
