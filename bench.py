@@ -188,14 +188,14 @@ def auto_single_launch(cfg, rank, reduce_path="contiguous", schedule="static"):
     import zero_sharded_state_amd as zs
     h = zs.zs3_layout_create(cfg.world_size, cfg.threshold, cfg.ds_ids, cfg.numels)
     try:
-        N = cfg.world_size
-        gather = 0
-        for b in zs.zs3_plan_buckets(h, zs.ZS3_GATHER_BUCKETS, cfg.prefetch_bucket_size):
-            gather += sum(4 * (zs.zs3_layout_own_range(h, d, rank)[1] - zs.zs3_layout_own_range(h, d, rank)[0])
-                          + 4 * zs.zs3_layout_param(h, d)["numel"] for d in b)
-        own = sum(zs.zs3_layout_own_range(h, d, rank)[1] - zs.zs3_layout_own_range(h, d, rank)[0]
-                  for d in cfg.ds_ids)
-        reduce = (2 * N + 2) * own
+        own = {}
+        for d in cfg.ds_ids:
+            lo, hi = zs.zs3_layout_own_range(h, d, rank)
+            own[d] = hi - lo
+        # pack 4 B per own element + unpack 4 B per gathered element, per pass
+        gather = sum(4 * own[d] + 4 * zs.zs3_layout_param(h, d)["numel"]
+                     for b in zs.zs3_plan_buckets(h, zs.ZS3_GATHER_BUCKETS, cfg.prefetch_bucket_size) for d in b)
+        reduce = (2 * cfg.world_size + 2) * sum(own.values())
     finally:
         zs.zs3_layout_destroy(h)
     g = schedule == "static" and gather < SINGLE_LAUNCH_BELOW_BYTES
